@@ -1,0 +1,77 @@
+"""O3: writing token K/V rows into physical slots, and reading a sequence back.
+
+Test infrastructure only (see the package docstring).
+
+A physical block holds the keys and values of B consecutive tokens of one
+sequence for every KV head ("PagedAttention -- Math + Memory Model", section
+"PagedAttention: blocks and the block table"; "KV-cache paging in vLLM",
+section "PagedAttention: Paging for KV-Caches").  The element order inside a
+block is the library's documented storage layout, restated here from its
+definition (x = 16 bytes / element size, so a 16-byte chunk of a key row is
+x elements):
+
+    key   pool  [num_blocks][n_kv_heads][head_dim / x][B][x]
+          element (blk, h, c, off, e) = key of token (blk, off), head h, dim c*x + e
+    value pool  [num_blocks][n_kv_heads][head_dim][B]
+          element (blk, h, d, off)    = value of token (blk, off), head h, dim d
+
+Slot s names token position s % B of physical block s // B.  Everything
+here moves raw bits (uint16 / uint32 / float32 arrays are copied, never
+converted), so -0.0 and NaN payloads survive.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def chunk_elems(esize: int) -> int:
+    return 16 // esize
+
+
+def empty_pools(num_blocks: int, n_kv_heads: int, head_dim: int, block_size: int,
+                storage_dtype, fill_bits: int):
+    """Key and value pools filled with one bit pattern (a NaN poison in parity runs)."""
+    esize = np.dtype(storage_dtype).itemsize
+    x = chunk_elems(esize)
+    k = np.empty((num_blocks, n_kv_heads, head_dim // x, block_size, x), dtype=storage_dtype)
+    v = np.empty((num_blocks, n_kv_heads, head_dim, block_size), dtype=storage_dtype)
+    ui = {2: np.uint16, 4: np.uint32}[esize]
+    k.view(ui)[...] = fill_bits
+    v.view(ui)[...] = fill_bits
+    return k, v
+
+
+def reshape_and_cache(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                      k_pool: np.ndarray, v_pool: np.ndarray) -> None:
+    """pool[slot // B, :, slot % B, :] = row[t] for every token t whose slot is in range.
+
+    Negative slots (padding tokens) and slots past the pool are skipped.
+    k, v: [T, Hk, D] in the pool's storage dtype.
+    """
+    N, Hk, C, B, x = k_pool.shape
+    T = k.shape[0]
+    assert k.shape == (T, Hk, C * x) and v.shape == (T, Hk, C * x)
+    for t in range(T):
+        s = int(slot_mapping[t])
+        if s < 0 or s >= N * B:
+            continue
+        blk, off = divmod(s, B)
+        k_pool[blk, :, :, off, :] = k[t].reshape(Hk, C, x)
+        v_pool[blk, :, :, off] = v[t]
+
+
+def gather_logical(k_pool: np.ndarray, v_pool: np.ndarray, table, L: int):
+    """A sequence's logical K and V, [L, Hk, D] each: position i is token i % B of block
+    table[i // B] ("PagedAttention -- Math + Memory Model", section "PagedAttention: blocks and
+    the block table").  Table entries past ceil(L/B) are never read."""
+    N, Hk, C, B, x = k_pool.shape
+    D = C * x
+    nb = -(-L // B)
+    ids = np.asarray(table[:nb], dtype=np.int64)
+    if nb and (ids.min() < 0 or ids.max() >= N):
+        raise IndexError("block table entry outside the pool")
+    kb = k_pool[ids]                       # [nb, Hk, C, B, x]
+    vb = v_pool[ids]                       # [nb, Hk, D, B]
+    K = kb.transpose(0, 3, 1, 2, 4).reshape(nb * B, Hk, D)[:L]
+    V = vb.transpose(0, 3, 1, 2).reshape(nb * B, Hk, D)[:L]
+    return np.ascontiguousarray(K), np.ascontiguousarray(V)
