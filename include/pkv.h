@@ -1,0 +1,261 @@
+/*
+ * libpagedkv -- paged KV cache for decode on AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache of every sequence lives in fixed-size physical blocks of B
+ * tokens taken from one device pool; a per-sequence block table maps
+ * logical block i (tokens i*B .. (i+1)*B-1) to the physical block that backs
+ * it, and blocks are handed out only when a sequence fills its last one
+ * ("PagedAttention -- Math + Memory Model", section "PagedAttention: blocks
+ * and the block table").  Decode attention follows that table and gathers
+ * the scattered blocks for QK^T, a numerically stable softmax and the
+ * value-weighted sum (same section; "KV-cache paging in vLLM", section "The
+ * Attention Kernel Change").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Return value: PKV_OK or a negative PKV_ERR_* code.  Argument checks run
+ *   before anything is launched or changed; a rejected call has no effect.
+ * - Device pointers are caller-owned.  The library never allocates device
+ *   memory: scratch space is the caller's workspace argument.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Launches are asynchronous on that stream; nothing here synchronises.
+ *   A failed launch returns PKV_ERR_HIP.
+ * - Element types: PKV_F32 (float), PKV_F16 (IEEE binary16), PKV_BF16
+ *   (bfloat16).  Copies move raw bits (NaN payloads and -0.0 survive).
+ * - Integer sizes are int32_t, token slots are int64_t.
+ *
+ * Storage layout of the pools (row-major, X = 16 bytes / element size, so X
+ * elements make one 16-byte vector):
+ *   key pool   [num_blocks][n_kv_heads][head_dim / X][block_size][X]
+ *   value pool [num_blocks][n_kv_heads][head_dim][block_size]
+ * One physical block holds all KV heads of its B tokens; the (block, head)
+ * chunk of each pool is block_size * head_dim elements, contiguous.  Slot s
+ * is token s % block_size of block s / block_size.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes and element types --------------------------------------- */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* a null pointer, size out of range, inconsistent shapes */
+  PKV_ERR_OOM = -2,         /* the allocator's pool has too few free blocks */
+  PKV_ERR_NOT_FOUND = -3,   /* unknown sequence id */
+  PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel for this head_dim / block_size / group */
+  PKV_ERR_HIP = -5          /* the HIP runtime reported an error */
+};
+
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+/* Kernel ids reported by pkv_timing_collect. */
+enum {
+  PKV_K_RESHAPE_AND_CACHE = 0,
+  PKV_K_APPEND_SLOTS = 1,
+  PKV_K_DECODE_PLAN = 2,
+  PKV_K_DECODE = 3,
+  PKV_K_DECODE_REDUCE = 4,
+  PKV_K_COUNT = 5
+};
+
+/* Text for a status code (static storage, never NULL). */
+const char* pkv_status_string(int status);
+
+/* Library ABI version, bumped on any incompatible change. */
+int pkv_version(void);
+
+/* Bytes of ONE pool (key or value) for the given shape; 0 if the shape is invalid. */
+size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t block_size, int dtype);
+
+/* ---- slot-mapping scatter ---------------------------------------------------
+ * Writes each new token's key and value rows into its physical slot:
+ *   for every token t with 0 <= slot_mapping[t] < num_blocks * block_size,
+ *     key pool   element (slot/B, h, d/X, slot%B, d%X) = k[t, h, d]
+ *     value pool element (slot/B, h, d,   slot%B)      = v[t, h, d]
+ * Negative slots (padding tokens) and slots past the pool are skipped.  The
+ * append of a token to its sequence's last block is what the block manager
+ * hands out slots for ("PagedAttention -- Math + Memory Model", section
+ * "PagedAttention: blocks and the block table"; "KV-Cache Optimization &
+ * PagedAttention for Long-Context Agents", section "Key KV-Cache Optimization
+ * Principles", item 1).
+ *   k, v          device, [num_tokens][n_kv_heads][head_dim] with a token stride
+ *                 of k_token_stride / v_token_stride elements (0 = n_kv_heads*head_dim;
+ *                 lets k and v be views into a fused QKV buffer; 16-byte aligned rows)
+ *   slot_mapping  device, int64 [num_tokens]
+ *   k_pool/v_pool device, pools of the documented layout
+ * Two tokens with the same slot in one call: undefined which one lands.
+ * Bits are copied unchanged.  head_dim must be a multiple of X. */
+int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                          int32_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                          void* k_pool, void* v_pool, int32_t num_blocks, int32_t n_kv_heads,
+                          int32_t head_dim, int32_t block_size, int dtype, void* stream);
+
+/* ---- device half of the on-demand append --------------------------------------
+ * One decode step appends one token per batch row.  For every row i with
+ * slot_mapping[i] >= 0, with p = seq_lens[i] (the new token's position):
+ *   block_tables[i * block_table_stride + p / block_size] = slot_mapping[i] / block_size
+ *   seq_lens[i] = p + 1
+ * i.e. the physical block the host allocator chose for position p is
+ * appended to (or kept in) the row's table ("PagedAttention -- Math + Memory
+ * Model", section "PagedAttention: blocks and the block table": a sequence
+ * that fills its last block gets one more from the pool, appended to its
+ * table).  Rows with a negative slot, a negative length or p / block_size >=
+ * block_table_stride are left unchanged.
+ *   slot_mapping  device int64 [num_seqs]
+ *   block_tables  device int32 [num_seqs][block_table_stride], updated in place
+ *   seq_lens      device int32 [num_seqs], updated in place */
+int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
+                     int32_t block_table_stride, int32_t* seq_lens, int32_t block_size,
+                     void* stream);
+
+/* ---- decode attention ---------------------------------------------------------
+ * For every batch row s and query head h (G = n_q_heads / n_kv_heads, KV head
+ * kv = h / G, L = seq_lens[s]):
+ *   x_j  = scale * <q[s,h,:], K_s[j,kv,:]>               j = 0 .. L-1
+ *   out[s,h,:] = sum_j exp(x_j - max x) V_s[j,kv,:] / sum_j exp(x_j - max x)
+ * where K_s[j] / V_s[j] is token j % B of physical block
+ * block_tables[s * block_table_stride + j / B].  Rows with L <= 0 get zeros.
+ *
+ * Work is split into partitions of partition_size tokens per (row, KV head);
+ * each partition keeps its running max, sum and fp32 accumulator, and rows
+ * with more than one partition are merged by log-sum-exp rescaling.
+ * Accumulation is fp32; for 16-bit KV with G >= 4 the products run on MFMA
+ * with the softmax weights rounded to the KV type (the denominator sums the
+ * same rounded weights).
+ *   out            device [num_seqs][n_q_heads][head_dim] of out_dtype
+ *                  (out_dtype = kv_dtype or PKV_F32; rounding to nearest even)
+ *   q              device [num_seqs][n_q_heads][head_dim] of kv_dtype, 16-byte aligned rows
+ *   k_pool, v_pool device pools of the documented layout
+ *   block_tables   device int32 [num_seqs][block_table_stride]; only the first
+ *                  ceil(L/B) entries of a row are read; an entry outside
+ *                  [0, num_blocks) is clamped into it (no fault; the row's result is
+ *                  then meaningless)
+ *   seq_lens       device int32 [num_seqs]; a length above max_seq_len is treated as
+ *                  max_seq_len
+ *   max_seq_len    host bound on seq_lens, sizes the workspace
+ *   partition_size tokens per partition: a positive multiple of 32, or 0 for
+ *                  "never split" (one partition of max_seq_len tokens)
+ *   workspace      device scratch of at least pkv_paged_attention_workspace_size()
+ *                  bytes, 256-byte aligned; its contents on entry do not matter; two
+ *                  calls in flight at once must not share it
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32; G = 1..16 for
+ * 16-bit KV (1..3 on the vector path, 4..16 on MFMA), G = 1..4 for fp32 KV. */
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t head_dim,
+                                          int32_t max_seq_len, int32_t partition_size);
+
+int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               int32_t block_table_stride, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               float scale, int32_t max_seq_len, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, int kv_dtype,
+                               void* stream);
+
+/* ---- host block allocator ------------------------------------------------------
+ * The block manager of the pages: a free list of physical block ids, a
+ * reference count per block, and per-sequence block tables.
+ *   - free list: blocks are taken from the head and returned to the tail, as
+ *     in the simulator of "KV-Cache Optimization & PagedAttention for
+ *     Long-Context Agents" (section "Python Implementation: Paged KV-Cache
+ *     Virtual Memory Simulator"); a freed sequence returns its blocks in
+ *     logical order;
+ *   - on-demand append: a new sequence owns zero blocks; position p takes a
+ *     fresh block when p % B == 0 ("PagedAttention -- Math + Memory Model",
+ *     section "PagedAttention: blocks and the block table");
+ *   - sharing and copy-on-write: pkv_fork points a child's first table entries
+ *     at the parent's blocks (reference count + 1 each); the first append into a
+ *     partly filled block that others still share takes a fresh block, reports
+ *     the (old, new) pair for the caller to copy, and drops the old block's count;
+ *     a block rejoins the pool when its count reaches zero (same page, section
+ *     "Copy-on-write: sharing blocks across samples").
+ * Host memory only; an allocator is not thread-safe (one caller at a time).
+ * Sequence ids are arbitrary int64 values chosen by the caller. */
+typedef struct pkv_allocator pkv_allocator;
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t free_blocks;
+  int32_t allocated_blocks; /* reference count > 0 */
+  int32_t shared_blocks;    /* reference count > 1 */
+  int32_t reserved;
+  int64_t num_seqs;
+  int64_t live_tokens;      /* sum of sequence lengths (a shared token counts per sequence) */
+  int64_t allocated_slots;  /* allocated_blocks * block_size */
+} pkv_stats;
+
+/* initial_free_order: NULL for 0..num_blocks-1, else a permutation of it (the
+ * order blocks are handed out in).  *out receives the new allocator. */
+int pkv_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                         pkv_allocator** out);
+void pkv_allocator_destroy(pkv_allocator* a);
+
+/* Appends n_new_tokens to seq_id (created with zero blocks if unknown).
+ * slots_out (nullable, n_new_tokens entries) receives each token's slot.
+ * cow_pair_out (nullable, 2 entries) receives [old, new] if the append copied a
+ * shared block; *n_cow (nullable) receives 0 or 1.  All or nothing: PKV_ERR_OOM
+ * leaves the allocator unchanged (and does not create seq_id). */
+int pkv_alloc(pkv_allocator* a, int64_t seq_id, int32_t n_new_tokens, int64_t* slots_out,
+              int32_t* cow_pair_out, int32_t* n_cow);
+
+/* pkv_alloc of n_new_each tokens for each of n_seqs distinct sequences, in order,
+ * as one all-or-nothing step.  slots_out (nullable) is [n_seqs][n_new_each];
+ * cow_pairs_out (nullable) has room for 2 * n_seqs ints and receives the copy
+ * pairs in order; *n_cow (nullable) their count.  Repeated ids: PKV_ERR_INVALID. */
+int pkv_alloc_batch(pkv_allocator* a, const int64_t* seq_ids, int32_t n_seqs, int32_t n_new_each,
+                    int64_t* slots_out, int32_t* cow_pairs_out, int32_t* n_cow);
+
+/* The child (which must not exist) shares the parent's first ceil(n/B) blocks and
+ * gets length n; n_shared_tokens = -1 shares the parent's whole length. */
+int pkv_fork(pkv_allocator* a, int64_t parent, int64_t child, int32_t n_shared_tokens);
+
+/* Drops seq_id; each of its blocks loses one reference, in logical order, and
+ * rejoins the tail of the free list at zero. */
+int pkv_free(pkv_allocator* a, int64_t seq_id);
+
+/* Copies up to cap table entries of seq_id to out (nullable); *n_blocks and
+ * *seq_len (nullable) receive the full table length and the sequence length. */
+int pkv_get_block_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
+                        int32_t* n_blocks, int32_t* seq_len);
+
+/* Packs the tables of a batch into tables[n_seqs][stride] (unused entries =
+ * pad_value) and their lengths into seq_lens (nullable).  PKV_ERR_INVALID if a
+ * table is longer than stride. */
+int pkv_fill_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32_t n_seqs,
+                          int32_t* tables, int32_t stride, int32_t pad_value, int32_t* seq_lens);
+
+int pkv_allocator_stats(const pkv_allocator* a, pkv_stats* out);
+
+/* Reference count of a block, or -1 for an id outside the pool. */
+int32_t pkv_block_ref_count(const pkv_allocator* a, int32_t block);
+
+/* The free list from head to tail: up to cap ids into out (nullable), *n = its length. */
+int pkv_free_list(const pkv_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+
+/* ---- kernel timing ----------------------------------------------------------------
+ * While enabled, every kernel launch of this library is bracketed by a pair of
+ * hipEvents recorded on its stream.  pkv_timing_collect waits for those events,
+ * writes one record per kernel id that ran (launch count and summed duration)
+ * and forgets them.  Enabling or disabling also forgets pending records. */
+typedef struct {
+  int32_t kernel;
+  int32_t launches;
+  double total_ms;
+} pkv_kernel_time;
+
+int pkv_timing_enable(int enable);
+int pkv_timing_collect(pkv_kernel_time* out, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -51,6 +51,8 @@ def reshape_and_cache(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
     N, Hk, C, B, x = k_pool.shape
     T = k.shape[0]
     assert k.shape == (T, Hk, C * x) and v.shape == (T, Hk, C * x)
+    # bits, not values: rows and pools must hold the same element type
+    assert k.dtype == k_pool.dtype and v.dtype == v_pool.dtype
     for t in range(T):
         s = int(slot_mapping[t])
         if s < 0 or s >= N * B:

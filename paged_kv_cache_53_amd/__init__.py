@@ -1,0 +1,244 @@
+"""libpagedkv: paged KV cache for decode on MI355X -- Python binding.
+
+Thin wrappers over the C ABI (include/pkv.h) that take torch tensors for
+device memory and torch's current stream; every step of the hot path runs in
+the HIP kernels of libpagedkv.so.  Nothing here computes on the CPU, and
+nothing falls back if the library is missing.
+
+    k_pool, v_pool = torch.empty(key_pool_shape(...)), torch.empty(value_pool_shape(...))
+    reshape_and_cache(k, v, slot_mapping, k_pool, v_pool)
+    paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale, max_seq_len)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import List, Optional, Sequence, Tuple
+
+from . import _lib
+from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PKV_ERR_OOM,  # noqa: F401
+                   PKV_ERR_UNSUPPORTED, PKV_F16, PKV_F32, PKV_OK, KERNEL_NAMES, LibraryNotBuilt)
+
+__all__ = [
+    "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
+    "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
+    "timing_enable", "timing_collect", "lib",
+]
+
+
+def lib():
+    return _lib.load()
+
+
+class PKVError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = lib().pkv_status_string(status).decode()
+        super().__init__(f"{what}: {msg} ({status})" if what else f"{msg} ({status})")
+
+
+class OutOfBlocks(PKVError, MemoryError):
+    pass
+
+
+def _check(status: int, what: str) -> None:
+    if status == PKV_OK:
+        return
+    if status == PKV_ERR_OOM:
+        raise OutOfBlocks(status, what)
+    raise PKVError(status, what)
+
+
+def dtype_code(t) -> int:
+    import torch
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    return {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}[dt]
+
+
+def _x(dtype) -> int:
+    import torch
+    return 16 // torch.empty((), dtype=dtype).element_size()
+
+
+def key_pool_shape(num_blocks: int, n_kv_heads: int, head_dim: int, block_size: int, dtype) -> Tuple[int, ...]:
+    """[num_blocks][n_kv_heads][head_dim / X][block_size][X], X = 16 bytes / element size."""
+    x = _x(dtype)
+    return (num_blocks, n_kv_heads, head_dim // x, block_size, x)
+
+
+def value_pool_shape(num_blocks: int, n_kv_heads: int, head_dim: int, block_size: int) -> Tuple[int, ...]:
+    """[num_blocks][n_kv_heads][head_dim][block_size]."""
+    return (num_blocks, n_kv_heads, head_dim, block_size)
+
+
+def pool_bytes(num_blocks, n_kv_heads, head_dim, block_size, dtype) -> int:
+    return int(lib().pkv_pool_bytes(num_blocks, n_kv_heads, head_dim, block_size, dtype_code(dtype)))
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _pool_dims(k_pool, v_pool):
+    if k_pool.dim() != 5 or v_pool.dim() != 4:
+        raise ValueError("k_pool must be [N, Hk, D/X, B, X] and v_pool [N, Hk, D, B]")
+    N, Hk, Cx, B, X = k_pool.shape
+    D = Cx * X
+    if tuple(v_pool.shape) != (N, Hk, D, B):
+        raise ValueError(f"value pool shape {tuple(v_pool.shape)} does not match key pool {tuple(k_pool.shape)}")
+    if not (k_pool.is_contiguous() and v_pool.is_contiguous()) or k_pool.dtype != v_pool.dtype:
+        raise ValueError("pools must be contiguous and of one dtype")
+    return N, Hk, D, B
+
+
+def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Writes k[t], v[t] ([T, Hk, D], token rows may be strided) into slot slot_mapping[t]."""
+    N, Hk, D, B = _pool_dims(k_pool, v_pool)
+    T = k.shape[0]
+    if k.shape != (T, Hk, D) or v.shape != (T, Hk, D) or slot_mapping.shape != (T,):
+        raise ValueError("k, v must be [T, Hk, D] and slot_mapping [T]")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError("k/v rows must be contiguous within a token")
+    _check(lib().pkv_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), T, k.stride(0), v.stride(0),
+                                       _ptr(k_pool), _ptr(v_pool), N, Hk, D, B, dtype_code(k_pool),
+                                       _stream(stream)), "pkv_reshape_and_cache")
+
+
+def append_slots(slot_mapping, block_tables, seq_lens, block_size: int, stream=None) -> None:
+    """Device half of a decode step's append: table[i][seq_lens[i] / B] = slot[i] / B; seq_lens[i] += 1."""
+    S = slot_mapping.shape[0]
+    _check(lib().pkv_append_slots(_ptr(slot_mapping), S, _ptr(block_tables), block_tables.stride(0),
+                                  _ptr(seq_lens), block_size, _stream(stream)), "pkv_append_slots")
+
+
+def workspace_size(num_seqs, n_q_heads, head_dim, max_seq_len, partition_size=512) -> int:
+    return int(lib().pkv_paged_attention_workspace_size(num_seqs, n_q_heads, head_dim, max_seq_len,
+                                                          partition_size))
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
+                           partition_size: int = 512, workspace=None, stream=None) -> None:
+    """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h)."""
+    import torch
+    N, Hk, D, B = _pool_dims(k_pool, v_pool)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [S, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [S, stride] with unit column stride")
+    need = workspace_size(S, Hq, D, max_seq_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_paged_attention_decode(
+        _ptr(out), dtype_code(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        block_tables.stride(0), _ptr(seq_lens), S, Hq, Hk, D, B, N, float(scale), int(max_seq_len),
+        int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        dtype_code(k_pool), _stream(stream)), "pkv_paged_attention_decode")
+
+
+def timing_enable(on: bool = True) -> None:
+    _check(lib().pkv_timing_enable(1 if on else 0), "pkv_timing_enable")
+
+
+def timing_collect() -> dict:
+    """{kernel name: (launches, total ms)} for launches since the last collect (waits for them)."""
+    recs = (_lib.pkv_kernel_time * 8)()
+    n = C.c_int32(0)
+    _check(lib().pkv_timing_collect(recs, 8, C.byref(n)), "pkv_timing_collect")
+    return {KERNEL_NAMES[recs[i].kernel]: (recs[i].launches, recs[i].total_ms) for i in range(n.value)}
+
+
+class Allocator:
+    """Host block allocator (pkv_allocator): FIFO free list, ref counts, fork, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order: Optional[Sequence[int]] = None):
+        self._h = C.c_void_p()
+        order = None
+        if initial_free_order is not None:
+            order = (C.c_int32 * num_blocks)(*[int(b) for b in initial_free_order])
+        _check(lib().pkv_allocator_create(num_blocks, block_size, order, C.byref(self._h)),
+               "pkv_allocator_create")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().pkv_allocator_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        slots = (C.c_int64 * max(n, 1))()
+        pair = (C.c_int32 * 2)()
+        ncow = C.c_int32(0)
+        _check(lib().pkv_alloc(self._h, seq, n, slots, pair, C.byref(ncow)), "pkv_alloc")
+        return list(slots[:n]), ([(pair[0], pair[1])] if ncow.value else [])
+
+    def alloc_batch(self, seqs: Sequence[int], n_each: int, slots_out=None):
+        """Appends n_each tokens to every sequence; slots_out: optional int64 numpy array [S*n_each]."""
+        import numpy as np
+        S = len(seqs)
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        if slots_out is None:
+            slots_out = np.empty(S * n_each, dtype=np.int64)
+        pairs = np.empty(2 * max(S, 1), dtype=np.int32)
+        ncow = C.c_int32(0)
+        _check(lib().pkv_alloc_batch(self._h, ids.ctypes.data_as(_lib.PI64), S, n_each,
+                                     slots_out.ctypes.data_as(_lib.PI64), pairs.ctypes.data_as(_lib.PI32),
+                                     C.byref(ncow)), "pkv_alloc_batch")
+        return slots_out, [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(ncow.value)]
+
+    def fork(self, parent: int, child: int, n: int = -1) -> None:
+        _check(lib().pkv_fork(self._h, parent, child, n), "pkv_fork")
+
+    def free(self, seq: int) -> None:
+        _check(lib().pkv_free(self._h, seq), "pkv_free")
+
+    def block_table(self, seq: int) -> List[int]:
+        nb, L = C.c_int32(0), C.c_int32(0)
+        _check(lib().pkv_get_block_table(self._h, seq, None, 0, C.byref(nb), C.byref(L)), "pkv_get_block_table")
+        buf = (C.c_int32 * max(nb.value, 1))()
+        _check(lib().pkv_get_block_table(self._h, seq, buf, nb.value, None, None), "pkv_get_block_table")
+        return list(buf[:nb.value])
+
+    def seq_len(self, seq: int) -> int:
+        nb, L = C.c_int32(0), C.c_int32(0)
+        _check(lib().pkv_get_block_table(self._h, seq, None, 0, C.byref(nb), C.byref(L)), "pkv_get_block_table")
+        return L.value
+
+    def fill_block_tables(self, seqs: Sequence[int], stride: int, pad: int = 0):
+        """(tables int32 [S, stride], seq_lens int32 [S]) as numpy arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        tables = np.empty((len(seqs), stride), dtype=np.int32)
+        lens = np.empty(len(seqs), dtype=np.int32)
+        _check(lib().pkv_fill_block_tables(self._h, ids.ctypes.data_as(_lib.PI64), len(seqs),
+                                           tables.ctypes.data_as(_lib.PI32), stride, pad,
+                                           lens.ctypes.data_as(_lib.PI32)), "pkv_fill_block_tables")
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = _lib.pkv_stats()
+        _check(lib().pkv_allocator_stats(self._h, C.byref(st)), "pkv_allocator_stats")
+        return {name: getattr(st, name) for name, _ in st._fields_ if name != "reserved"}
+
+    def ref_count(self, block: int) -> int:
+        return int(lib().pkv_block_ref_count(self._h, block))
+
+    def free_list(self) -> List[int]:
+        n = C.c_int32(0)
+        _check(lib().pkv_free_list(self._h, None, 0, C.byref(n)), "pkv_free_list")
+        buf = (C.c_int32 * max(n.value, 1))()
+        _check(lib().pkv_free_list(self._h, buf, n.value, None), "pkv_free_list")
+        return list(buf[:n.value])

@@ -1,0 +1,342 @@
+// C-ABI entry points of libpagedkv: argument checks, workspace carve-up, kernel dispatch,
+// and the optional per-kernel event timing.  Every check runs before anything is launched.
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline int esize(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+inline bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int log2i(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+// ---- kernel timing -----------------------------------------------------------------
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimingRecord> pending;
+  std::vector<hipEvent_t> spare;
+  hipEvent_t open_start = nullptr;  // recorded by timing_before, closed by timing_after
+  int open_kernel = -1;
+
+  hipEvent_t take() {
+    if (!spare.empty()) {
+      hipEvent_t e = spare.back();
+      spare.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void give(hipEvent_t e) {
+    if (e) spare.push_back(e);
+  }
+  void drop_pending() {
+    for (auto& r : pending) {
+      give(r.start);
+      give(r.stop);
+    }
+    pending.clear();
+    give(open_start);
+    open_start = nullptr;
+  }
+};
+
+Timing& timing() {
+  static Timing* t = new Timing();  // lives until process exit; events are never destroyed
+  return *t;
+}
+
+// ---- persistent-grid cap cache per (device, kernel variant) ---------------------------
+std::mutex cap_mu;
+std::unordered_map<int64_t, int32_t> cap_cache;
+
+hipError_t grid_cap(int dtype, int head_dim, int path, int group, int32_t* cap) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 2 + path) * 2) +
+                      (group == 1 ? 0 : 1);
+  {
+    std::lock_guard<std::mutex> g(cap_mu);
+    auto it = cap_cache.find(key);
+    if (it != cap_cache.end()) {
+      *cap = it->second;
+      return hipSuccess;
+    }
+  }
+  e = decode_main_grid_cap(dtype, head_dim, path, group, cap);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(cap_mu);
+  cap_cache[key] = *cap;
+  return hipSuccess;
+}
+
+}  // namespace
+
+void timing_before(int kernel, hipStream_t stream) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.enabled) return;
+  t.give(t.open_start);
+  t.open_start = t.take();
+  t.open_kernel = kernel;
+  if (t.open_start && hipEventRecord(t.open_start, stream) != hipSuccess) {
+    t.give(t.open_start);
+    t.open_start = nullptr;
+  }
+}
+
+void timing_after(int kernel, hipStream_t stream) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.enabled || !t.open_start || t.open_kernel != kernel) return;
+  hipEvent_t stop = t.take();
+  if (stop && hipEventRecord(stop, stream) == hipSuccess) {
+    t.pending.push_back({kernel, t.open_start, stop});
+  } else {
+    t.give(t.open_start);
+    t.give(stop);
+  }
+  t.open_start = nullptr;
+}
+
+int32_t partition_tokens(int32_t max_seq_len, int32_t partition_size) {
+  if (partition_size > 0) return partition_size;
+  const int32_t L = max_seq_len > 0 ? max_seq_len : 1;
+  return (L + 31) / 32 * 32;
+}
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t n_q_heads, int32_t head_dim, int32_t max_parts) {
+  WorkspaceLayout w{};
+  const size_t units = static_cast<size_t>(num_seqs) * max_parts;
+  const size_t parts = units * n_q_heads;
+  w.counters_off = 0;
+  w.units_off = 256;
+  w.m_off = round_up(w.units_off + units * sizeof(int2), 256);
+  w.l_off = round_up(w.m_off + parts * sizeof(float), 256);
+  w.acc_off = round_up(w.l_off + parts * sizeof(float), 256);
+  w.total = round_up(w.acc_off + parts * head_dim * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_OOM: return "out of KV-cache blocks";
+    case PKV_ERR_NOT_FOUND: return "unknown sequence";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 1; }
+
+size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                      int dtype) {
+  if (num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || !valid_dtype(dtype))
+    return 0;
+  const int X = 16 / esize(dtype);
+  if (head_dim % X) return 0;
+  return static_cast<size_t>(num_blocks) * n_kv_heads * head_dim * block_size * esize(dtype);
+}
+
+int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                          int64_t k_token_stride, int64_t v_token_stride, void* k_pool, void* v_pool,
+                          int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                          int dtype, void* stream) {
+  if (num_tokens < 0 || !valid_dtype(dtype) || num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0)
+    return PKV_ERR_INVALID;
+  const int es = esize(dtype);
+  const int X = 16 / es;
+  if (head_dim % X) return PKV_ERR_INVALID;
+  const int64_t row = static_cast<int64_t>(n_kv_heads) * head_dim;
+  const int64_t ks = k_token_stride == 0 ? row : k_token_stride;
+  const int64_t vs = v_token_stride == 0 ? row : v_token_stride;
+  if (ks < row || vs < row || (ks * es) % 16 || (vs * es) % 16) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_INVALID;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID;
+  ScatterArgs a{k, v, slot_mapping, k_pool, v_pool, ks, vs, num_tokens, num_blocks, n_kv_heads,
+                head_dim, block_size};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_RESHAPE_AND_CACHE, st);
+  const hipError_t e = launch_reshape_and_cache(a, dtype, st);
+  timing_after(PKV_K_RESHAPE_AND_CACHE, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
+                     int32_t block_table_stride, int32_t* seq_lens, int32_t block_size, void* stream) {
+  if (num_seqs < 0 || block_table_stride <= 0 || block_size <= 0) return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!slot_mapping || !block_tables || !seq_lens) return PKV_ERR_INVALID;
+  if (!aligned(slot_mapping, 8) || !aligned(block_tables, 4) || !aligned(seq_lens, 4)) return PKV_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_APPEND_SLOTS, st);
+  const hipError_t e = launch_append_slots(slot_mapping, num_seqs, block_tables, block_table_stride,
+                                           seq_lens, block_size, st);
+  timing_after(PKV_K_APPEND_SLOTS, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t head_dim,
+                                          int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs < 0 || n_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size < 0 ||
+      (partition_size % 32))
+    return 0;
+  const int32_t P = partition_tokens(max_seq_len, partition_size);
+  const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
+  return workspace_layout(num_seqs, n_q_heads, head_dim, max_parts).total;
+}
+
+int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, int kv_dtype, void* stream) {
+  // ---- shape and type checks
+  if (!valid_dtype(kv_dtype) || !(out_dtype == kv_dtype || out_dtype == PKV_F32)) return PKV_ERR_INVALID;
+  if (num_seqs < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || (n_q_heads % n_kv_heads) || num_blocks <= 0 ||
+      max_seq_len < 0 || partition_size < 0 || (partition_size % 32) || block_size <= 0 ||
+      !(scale == scale))
+    return PKV_ERR_INVALID;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int group = n_q_heads / n_kv_heads;
+  int path;
+  if (kv_dtype == PKV_F32) {
+    if (group > 4) return PKV_ERR_UNSUPPORTED;
+    path = 0;
+  } else {
+    if (group > 16) return PKV_ERR_UNSUPPORTED;
+    path = group >= 4 ? 1 : 0;
+  }
+  const int64_t max_blocks = (static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size;
+  if (block_table_stride < max_blocks || block_table_stride < 0) return PKV_ERR_INVALID;
+  const int32_t P = partition_tokens(max_seq_len, partition_size);
+  const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
+  const int64_t unit_bound = static_cast<int64_t>(num_seqs) * max_parts * n_kv_heads;
+  if (unit_bound >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  // ---- pointer checks
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !workspace) return PKV_ERR_INVALID;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 256))
+    return PKV_ERR_INVALID;
+  const WorkspaceLayout wl = workspace_layout(num_seqs, n_q_heads, head_dim, max_parts);
+  if (workspace_bytes < wl.total) return PKV_ERR_INVALID;
+
+  char* ws = static_cast<char*>(workspace);
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.counters = reinterpret_cast<int32_t*>(ws + wl.counters_off);
+  a.units = reinterpret_cast<int2*>(ws + wl.units_off);
+  a.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+  a.part_l = reinterpret_cast<float*>(ws + wl.l_off);
+  a.part_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+  a.bt_stride = block_table_stride;
+  a.num_seqs = num_seqs;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.log2_block = log2i(block_size);
+  a.max_seq_len = max_seq_len;
+  a.part_tokens = P;
+  a.max_parts = max_parts;
+  a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  int32_t cap = 0;
+  if (grid_cap(kv_dtype, head_dim, path, group, &cap) != hipSuccess) return PKV_ERR_HIP;
+  const int32_t grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_DECODE_PLAN, st);
+  hipError_t e = launch_decode_plan(a, kv_dtype, head_dim, st);
+  timing_after(PKV_K_DECODE_PLAN, st);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  timing_before(PKV_K_DECODE, st);
+  e = launch_decode_main(a, kv_dtype, head_dim, path, grid, st);
+  timing_after(PKV_K_DECODE, st);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  if (max_parts > 1) {
+    timing_before(PKV_K_DECODE_REDUCE, st);
+    e = launch_decode_reduce(a, kv_dtype, head_dim, st);
+    timing_after(PKV_K_DECODE_REDUCE, st);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+int pkv_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.drop_pending();
+  t.enabled = enable != 0;
+  return PKV_OK;
+}
+
+int pkv_timing_collect(pkv_kernel_time* out, int32_t cap, int32_t* n) {
+  if (cap < 0 || (cap > 0 && !out)) return PKV_ERR_INVALID;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  double total[PKV_K_COUNT] = {0};
+  int32_t count[PKV_K_COUNT] = {0};
+  int status = PKV_OK;
+  for (auto& r : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      status = PKV_ERR_HIP;
+      continue;
+    }
+    total[r.kernel] += ms;
+    count[r.kernel] += 1;
+  }
+  t.drop_pending();
+  int32_t m = 0;
+  for (int k = 0; k < PKV_K_COUNT; ++k) {
+    if (!count[k]) continue;
+    if (m < cap) out[m] = pkv_kernel_time{k, count[k], total[k]};
+    ++m;
+  }
+  if (n) *n = m;
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal declarations shared by the HIP sources of libpagedkv (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------- launch parameters
+struct ScatterArgs {
+  const void* k;
+  const void* v;
+  const int64_t* slot_mapping;
+  void* k_pool;
+  void* v_pool;
+  int64_t k_stride;      // elements between consecutive tokens of k
+  int64_t v_stride;
+  int32_t num_tokens;
+  int32_t num_blocks;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  // workspace views
+  int32_t* counters;     // [0] = number of (row, partition) units, [1] = next unit to hand out
+  int2* units;           // (row, partition) pairs, row-major, partitions ascending
+  float* part_m;         // [S][Hq][max_parts]  running max of x*log2(e)
+  float* part_l;         // [S][Hq][max_parts]  sum of weights
+  float* part_acc;       // [S][Hq][max_parts][D]  unnormalised weighted V
+  int32_t bt_stride;
+  int32_t num_seqs;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;         // n_q_heads / n_kv_heads
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t log2_block;
+  int32_t max_seq_len;
+  int32_t part_tokens;   // partition size in tokens (multiple of 32)
+  int32_t max_parts;
+  int32_t out_f32;       // 1: out is float, 0: out has the KV type
+  float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
+};
+
+// Workspace carve-up shared by the size query and the launcher.
+struct WorkspaceLayout {
+  size_t counters_off, units_off, m_off, l_off, acc_off, total;
+};
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t n_q_heads, int32_t head_dim,
+                                 int32_t max_parts);
+int32_t partition_tokens(int32_t max_seq_len, int32_t partition_size);
+
+// ---------------------------------------------------------------- launchers (return hipError_t)
+hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
+                               int32_t stride, int32_t* seq_lens, int32_t block_size,
+                               hipStream_t stream);
+hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// path: 0 = vector, 1 = MFMA
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path,
+                              int32_t grid, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Persistent grid size for the main decode kernel on the current device.
+hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int32_t* cap);
+
+// ---------------------------------------------------------------- timing hooks
+void timing_before(int kernel, hipStream_t stream);
+void timing_after(int kernel, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,116 @@
+"""The decode-step runtime around the kernels: device pools + host allocator, and a batch.
+
+PagedKVCache   one layer's key/value pools on the device and the host block allocator that
+               hands out their slots (prompt writes go allocator -> scatter kernel).
+DecodeBatch    a fixed set of sequences decoded together: device block tables and lengths,
+               a workspace, and ``step()`` -- one decode step of the whole hot path:
+                 1. host: the allocator appends one token to every sequence (C++, one call)
+                 2. the new slots go to the device through a pinned, double-buffered stage
+                 3. append_slots kernel: new block ids into the device tables, lengths + 1
+                 4. reshape_and_cache kernel: the new tokens' K/V into their slots
+                 5. paged decode (plan, main, merge kernels)
+               Host work for step i+1 overlaps the GPU work of step i; the host waits only
+               before reusing a staging buffer that a copy may still be reading.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (Allocator, append_slots, key_pool_shape, paged_attention_decode, reshape_and_cache,
+               value_pool_shape, workspace_size)
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, block_size: int, n_kv_heads: int, head_dim: int, dtype,
+                 device="cuda", free_order: Optional[Sequence[int]] = None, fill: str = "zero"):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.n_kv_heads, self.head_dim, self.dtype, self.device = n_kv_heads, head_dim, dtype, device
+        self.allocator = Allocator(num_blocks, block_size, free_order)
+        ks = key_pool_shape(num_blocks, n_kv_heads, head_dim, block_size, dtype)
+        vs = value_pool_shape(num_blocks, n_kv_heads, head_dim, block_size)
+        if fill == "randn":
+            self.k_pool = torch.randn(ks, device=device, dtype=torch.float32).to(dtype)
+            self.v_pool = torch.randn(vs, device=device, dtype=torch.float32).to(dtype)
+        elif fill == "nan":
+            self.k_pool = torch.full(ks, float("nan"), device=device, dtype=dtype)
+            self.v_pool = torch.full(vs, float("nan"), device=device, dtype=dtype)
+        elif fill == "zero":
+            self.k_pool = torch.zeros(ks, device=device, dtype=dtype)
+            self.v_pool = torch.zeros(vs, device=device, dtype=dtype)
+        else:
+            raise ValueError(fill)
+
+    def append(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Appends len(k) tokens to seq: slots from the allocator, rows written by the scatter kernel."""
+        slots, pairs = self.allocator.alloc(seq, int(k.shape[0]))
+        if pairs:
+            raise NotImplementedError("copy-on-write block copies are not supported by this runtime yet")
+        if slots:
+            reshape_and_cache(k, v, torch.tensor(slots, dtype=torch.int64, device=self.device),
+                              self.k_pool, self.v_pool)
+
+    def fork(self, parent: int, child: int, n_tokens: int = -1) -> None:
+        self.allocator.fork(parent, child, n_tokens)
+
+    def free(self, seq: int) -> None:
+        self.allocator.free(seq)
+
+
+class DecodeBatch:
+    def __init__(self, cache: PagedKVCache, seq_ids: Sequence[int], n_q_heads: int, max_seq_len: int,
+                 partition_size: int = 512, scale: Optional[float] = None):
+        self.cache = cache
+        self.seq_ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        self.S = len(self.seq_ids)
+        self.n_q_heads = n_q_heads
+        self.max_seq_len = max_seq_len
+        self.partition_size = partition_size
+        self.scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else scale
+        B = cache.block_size
+        self.stride = max(1, -(-max_seq_len // B))
+        tables, lens = cache.allocator.fill_block_tables(self.seq_ids, self.stride, pad=0)
+        if int(lens.max(initial=0)) > max_seq_len:
+            raise ValueError("a sequence is already longer than max_seq_len")
+        dev = cache.device
+        self.tables = torch.from_numpy(tables).to(dev)
+        self.seq_lens = torch.from_numpy(lens.copy()).to(dev)
+        self.host_lens = lens.astype(np.int64)
+        self.workspace = torch.empty(max(256, workspace_size(self.S, n_q_heads, cache.head_dim, max_seq_len,
+                                                               partition_size)), dtype=torch.uint8, device=dev)
+        self.slot_stage = [torch.empty(self.S, dtype=torch.int64, pin_memory=True) for _ in range(2)]
+        self.slot_stage_np = [t.numpy() for t in self.slot_stage]
+        self.stage_done = [None, None]
+        self.slot_dev = torch.empty(self.S, dtype=torch.int64, device=dev)
+        self.steps = 0
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor) -> None:
+        """One decode step for every row: append the new token, write its K/V, attend over all tokens."""
+        if int(self.host_lens.max(initial=0)) + 1 > self.max_seq_len:
+            raise ValueError("decode step would exceed max_seq_len")
+        i = self.steps & 1
+        if self.stage_done[i] is not None:
+            self.stage_done[i].synchronize()          # the copy that last read this stage is done
+        _, pairs = self.cache.allocator.alloc_batch(self.seq_ids, 1, slots_out=self.slot_stage_np[i])
+        if pairs:
+            raise NotImplementedError("copy-on-write block copies are not supported by this runtime yet")
+        self.host_lens += 1
+        self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.stage_done[i] = ev
+        c = self.cache
+        append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
+        reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool)
+        paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
+                               self.max_seq_len, self.partition_size, workspace=self.workspace)
+        self.steps += 1
+
+    def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
+        """Attention over the current tokens without appending (no host work, no scatter)."""
+        c = self.cache
+        paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
+                               self.max_seq_len, self.partition_size, workspace=self.workspace)
