@@ -48,12 +48,14 @@ def parse():
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--block-size", type=int, default=None)
     p.add_argument("--placement", default="random", choices=["random", "identity"])
-    p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--partition-size", type=int, default=None, help="default: the workload's own")
     p.add_argument("--copied-prefix", action="store_true", help="config 4: private prefix copies")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--sweep", action="store_true", help="config-5 block-size x placement sweep (decode only)")
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -221,6 +223,15 @@ def main():
 
     if args.sweep:
         return sweep(args)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
+        return
 
     w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
                  copied_prefix=args.copied_prefix, partition_size=args.partition_size)
@@ -262,7 +273,7 @@ def sweep(args):
     for B in (8, 16, 32):
         per = {}
         for placement in ("random", "identity"):
-            w = wl.build(5, block_size=B, placement=placement, partition_size=args.partition_size)
+            w = wl.build(5, block_size=B, placement=placement, partition_size=args.partition_size or 512)
             res = time_steps(w, args.steps, args.warmup, decode_only=True)
             rf = roofline(res)
             n, ms = res["kernels"]["decode"]

@@ -54,6 +54,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         obj = os.path.join(BUILD, src + ".o")
         cmds.append([hipcc, f"--offload-arch={ARCH}", *common,
                      "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                     # keep a wave's work-claim atomic as written: the optimiser's rewrite reads the
+                     # result at once, making the wave wait for all of its outstanding loads
+                     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                      "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:

@@ -67,12 +67,12 @@ Timing& timing() {
 std::mutex cap_mu;
 std::unordered_map<int64_t, int32_t> cap_cache;
 
-hipError_t grid_cap(int dtype, int head_dim, int path, int group, int32_t* cap) {
+hipError_t grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 2 + path) * 2) +
-                      (group == 1 ? 0 : 1);
+  const int64_t key = (((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 2 + path) * 2) +
+                       (group == 1 ? 0 : 1)) * 64 + block_size;
   {
     std::lock_guard<std::mutex> g(cap_mu);
     auto it = cap_cache.find(key);
@@ -81,7 +81,7 @@ hipError_t grid_cap(int dtype, int head_dim, int path, int group, int32_t* cap) 
       return hipSuccess;
     }
   }
-  e = decode_main_grid_cap(dtype, head_dim, path, group, cap);
+  e = decode_main_grid_cap(dtype, head_dim, path, group, block_size, cap);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> g(cap_mu);
   cap_cache[key] = *cap;
@@ -225,7 +225,8 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                void* workspace, size_t workspace_bytes, int kv_dtype, void* stream) {
   // ---- shape and type checks
   if (!valid_dtype(kv_dtype) || !(out_dtype == kv_dtype || out_dtype == PKV_F32)) return PKV_ERR_INVALID;
-  if (num_seqs < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || (n_q_heads % n_kv_heads) || num_blocks <= 0 ||
+  if (num_seqs < 0 || n_q_heads <= 0 || n_q_heads > 65535 || n_kv_heads <= 0 || (n_q_heads % n_kv_heads) ||
+      num_blocks <= 0 ||
       max_seq_len < 0 || partition_size < 0 || (partition_size % 32) || block_size <= 0 ||
       !(scale == scale))
     return PKV_ERR_INVALID;
@@ -283,7 +284,7 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
   a.scale_log2 = scale * 1.4426950408889634f;
 
   int32_t cap = 0;
-  if (grid_cap(kv_dtype, head_dim, path, group, &cap) != hipSuccess) return PKV_ERR_HIP;
+  if (grid_cap(kv_dtype, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
   const int32_t grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
 
   hipStream_t st = static_cast<hipStream_t>(stream);

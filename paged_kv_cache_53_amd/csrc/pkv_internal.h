@@ -73,7 +73,7 @@ hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int 
                               int32_t grid, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.
-hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int32_t* cap);
+hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap);
 
 // ---------------------------------------------------------------- timing hooks
 void timing_before(int kernel, hipStream_t stream);

@@ -72,6 +72,7 @@ class DecodeBatch:
         self.scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else scale
         B = cache.block_size
         self.stride = max(1, -(-max_seq_len // B))
+        cache.allocator.alloc_batch(self.seq_ids, 0)      # sequences with no prompt exist, empty
         tables, lens = cache.allocator.fill_block_tables(self.seq_ids, self.stride, pad=0)
         if int(lens.max(initial=0)) > max_seq_len:
             raise ValueError("a sequence is already longer than max_seq_len")

@@ -151,7 +151,7 @@ def _independent(cid, name, seed, hq, hk, d, bsz, dtype, lens, free_order, n_blo
 
 def build(config_id: int, *, small: bool = False, block_size: Optional[int] = None,
           placement: str = "random", copied_prefix: bool = False,
-          partition_size: int = 512) -> Workload:
+          partition_size: Optional[int] = None) -> Workload:
     """The seeded workload for config 1..5 (seed = config_id - 1).
 
     ``small`` keeps the config's heads, head_dim, dtype, block size and length
@@ -169,7 +169,7 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
         bsz = block_size or 16
         return _independent(1, name, seed, 4, 4, 64, bsz, "f32", [1, 17, 33, 100],
                             _free_order(rng_place, 64, placement), 64, placement, variant,
-                            partition_size)
+                            partition_size or 512)
 
     if config_id == 2:
         # OPT-13B-class layer: 40 MHA heads x 128, fp16, B=16, lengths U[128, 2048], 8192 blocks.
@@ -182,7 +182,7 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
             n_blocks = 8192
         return _independent(2, name, seed, 40, 40, 128, bsz, "f16", lens,
                             _free_order(rng_place, n_blocks, placement), n_blocks,
-                            placement, variant, partition_size)
+                            placement, variant, partition_size or 512)
 
     if config_id == 3:
         # Llama-3-70B-class layer: 64 q / 8 kv heads, D=128, bf16, B=16, 256 sequences with
@@ -195,9 +195,11 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
             raw = rng_len.lognormal(mean=math.log(3000.0), sigma=1.0, size=256)
             lens = np.clip(np.rint(raw), 16, 32768).astype(np.int32)
         n_blocks = _pool_size([_ceil_div(int(L), bsz) for L in lens], 1.1)
+        # 1024-token partitions: half the partial results of 512 at 20k+ work units, which
+        # measured fastest for this length mix (the partition size is a launch choice)
         return _independent(3, name, seed, 64, 8, 128, bsz, "bf16", lens,
                             _free_order(rng_place, n_blocks, placement), n_blocks,
-                            placement, variant, partition_size)
+                            placement, variant, 1024 if partition_size is None else partition_size)
 
     if config_id == 4:
         # Agent swarm: 20 sequences share one 4000-token prompt (250 blocks), then private
@@ -230,7 +232,7 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
                         head_dim=128, block_size=bsz, dtype="f16", num_blocks=n_blocks,
                         free_order=_free_order(rng_place, n_blocks, placement),
                         prompt_ops=ops, batch=np.arange(n_children, dtype=np.int64),
-                        seq_lens=lens, segments=segs, partition_size=partition_size,
+                        seq_lens=lens, segments=segs, partition_size=partition_size or 512,
                         placement=placement,
                         variant=variant + ("-copied" if copied_prefix else "-shared"))
 
@@ -242,7 +244,7 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
         n_blocks = _pool_size([_ceil_div(L, bsz)] * n_seqs, 1.1)
         return _independent(5, name, seed, 64, 8, 128, bsz, "bf16", lens,
                             _free_order(rng_place, n_blocks, placement), n_blocks,
-                            placement, variant, partition_size)
+                            placement, variant, partition_size or 512)
 
     raise ValueError(f"unknown config {config_id}")
 
