@@ -147,7 +147,7 @@ def roofline(res):
     achieved = per_launch / avg_s / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-            "kernel": "decode_mfma_kernel / decode_vec_kernel (pkv decode main)",
+            "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV with G >= 3)",
             "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
 
 

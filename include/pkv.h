@@ -126,7 +126,7 @@ int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* blo
  * Work is split into partitions of partition_size tokens per (row, KV head);
  * each partition keeps its running max, sum and fp32 accumulator, and rows
  * with more than one partition are merged by log-sum-exp rescaling.
- * Accumulation is fp32; for 16-bit KV with G >= 4 the products run on MFMA
+ * Accumulation is fp32; for 16-bit KV with G >= 3 the products run on MFMA
  * with the softmax weights rounded to the KV type (the denominator sums the
  * same rounded weights).
  *   out            device [num_seqs][n_q_heads][head_dim] of out_dtype

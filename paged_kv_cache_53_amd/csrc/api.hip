@@ -71,8 +71,10 @@ hipError_t grid_cap(int dtype, int head_dim, int path, int group, int block_size
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int64_t key = (((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 2 + path) * 2) +
-                       (group == 1 ? 0 : 1)) * 64 + block_size;
+  // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4)
+  const int variant = path == 1 ? 3 : (group == 1 ? 0 : group == 2 ? 1 : 2);
+  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 4 + variant) * 64) +
+                      block_size;
   {
     std::lock_guard<std::mutex> g(cap_mu);
     auto it = cap_cache.find(key);
@@ -239,7 +241,7 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
     path = 0;
   } else {
     if (group > 16) return PKV_ERR_UNSUPPORTED;
-    path = group >= 4 ? 1 : 0;
+    path = group >= 3 ? 1 : 0;
   }
   const int64_t max_blocks = (static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size;
   if (block_table_stride < max_blocks || block_table_stride < 0) return PKV_ERR_INVALID;

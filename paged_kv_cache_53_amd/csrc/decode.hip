@@ -10,32 +10,42 @@
 //
 // How (MI355X design):
 // * Work unit = (row, KV head, partition of part_tokens tokens).  A one-workgroup
-//   plan kernel lists the (row, partition) pairs; a persistent grid of
-//   single-wave workgroups takes units from an atomic counter, so no
-//   workgroup is launched for a partition that does not exist and long and
-//   short rows balance across the 256 CUs.
-// * A wave walks its partition in tiles of 32 tokens (MFMA path) or 16 tokens
-//   (vector path).  The partition's block ids are read once, one per lane,
-//   and each lane picks the id of its token's block with ds_bpermute.
+//   plan kernel lists the (row, partition) pairs longest first; a persistent grid
+//   of single-wave workgroups takes units from one atomic counter, so no wave is
+//   launched for a partition that does not exist and long and short rows balance
+//   across the 256 CUs.
+// * A wave streams its units in 16-token tiles through three register buffers,
+//   two tiles in flight: while tile t is computed, tiles t+1 and t+2 are loading.
+//   The issue side runs ahead across unit boundaries (it claims the next unit a
+//   few tiles before the current one ends and loads that unit's q), so HBM sees
+//   no gap between units.  When nothing real is left to issue it issues filler
+//   loads of an already-loaded tile, which keeps the number of loads per step
+//   fixed: the compiler's wait before a tile's use then covers that tile only.
+// * Block ids, lengths and the unit list are read with scalar loads, which wait
+//   on their own counter and never stall behind the vector loads.
 // * Key rows are stored as 16-byte vectors [c][token][X]: the 64 lanes of a
 //   wave read 1 KiB contiguous per load (lane = token within 16, lane group =
-//   vector column).  Values are stored [dim][token] so that a lane's 4 or 8
-//   consecutive tokens of one dimension are one 8- or 16-byte load -- exactly
-//   the operand the PV product contracts over.
-// * MFMA path (16-bit KV, G >= 4): S^T = K q^T and O^T = V^T P^T with
-//   v_mfma_f32_16x16x32_{bf16,f16}; the G query heads of a KV head are the
-//   16-wide N dimension (zero-padded).  The QK accumulator layout (lane holds
-//   tokens 4g..4g+3 of each 16-token half for head lane%16) is exactly the B
-//   operand layout of the PV product, so weights never leave their lanes.
+//   vector column).  Values are stored [dim][token] so that a lane's 4
+//   consecutive tokens of one dimension are one 8-byte load -- exactly the
+//   operand the PV product contracts over.
+// * MFMA path (16-bit KV, G >= 3): S^T = K q^T and O^T = V^T P^T with
+//   v_mfma_f32_16x16x32_{bf16,f16} and v_mfma_f32_16x16x16{bf16_1k,f16}; the G
+//   query heads of a KV head are the 16-wide N dimension (padded).  The QK
+//   accumulator layout (lane holds tokens 4g..4g+3 for head lane%16) is exactly
+//   the B operand layout of the PV product, so weights never leave their lanes.
 //   The weights are rounded to the KV type for the PV operand, and the
 //   denominator sums the rounded values.
-// * Vector path (fp32 KV, or G < 4): per-token dot products with a 4-lane
+// * Vector path (fp32 KV, or G <= 2): per-token dot products with a 4-lane
 //   cross-group reduction, fp32 weights, FMA accumulation.
+// * q fragments live in LDS (one slot for the unit being computed, one for the
+//   unit being issued), so the tile buffers keep the registers.
 // * Online softmax in the base-2 domain (scores pre-multiplied by
 //   scale*log2(e), v_exp_f32); masked tokens get -inf scores and zeroed value
 //   elements (selected, never multiplied, so a NaN in an unused slot cannot
 //   leak in).  Rows with one partition write the output directly; longer rows
 //   write (max, sum, acc) partials that the reduce kernel merges.
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -98,14 +108,6 @@ __device__ inline int row_len(const DecodeArgs& a, int s) {
   return L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
 }
 
-// Next unit for this wave, or -1 when the list is exhausted.
-__device__ inline int next_unit(const DecodeArgs& a, int total) {
-  int u = 0;
-  if (threadIdx.x == 0) u = atomicAdd(&a.counters[1], 1);
-  u = __builtin_amdgcn_readfirstlane(u);
-  return u < total ? u : -1;
-}
-
 // ------------------------------------------------------------------------------ plan
 // Lists the (row, partition) pairs, largest first: every full partition, then each row's
 // shorter last partition in decreasing length (counting sort over 16-token buckets).  Waves
@@ -141,19 +143,25 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
     sums[tid] += v;
     __syncthreads();
   }
-  const int full_total = sums[1023];
-  // bucket bases, longest bucket first, after all full partitions (one thread: <= 1024 adds)
-  if (tid == 0) {
-    int acc = full_total;
-    for (int bk = NBUCKET - 1; bk >= 0; --bk) {
-      bucket_base[bk] = acc;
-      acc += bucket_fill[bk];
-      bucket_fill[bk] = 0;
-    }
-    a.counters[0] = acc;
-  }
-  __syncthreads();
   int off = sums[tid] - full_local;
+  const int full_total = sums[1023];
+  // bucket bases, longest bucket first, after all full partitions: an exclusive scan of the
+  // bucket counts taken in descending bucket order (thread t holds bucket NBUCKET-1-t)
+  const int rb = NBUCKET - 1 - tid;
+  const int cnt = bucket_fill[rb];
+  __syncthreads();
+  sums[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? sums[tid - d] : 0;
+    __syncthreads();
+    sums[tid] += v;
+    __syncthreads();
+  }
+  bucket_base[rb] = full_total + sums[tid] - cnt;
+  bucket_fill[rb] = 0;
+  if (tid == 1023) a.counters[0] = full_total + sums[1023];
+  __syncthreads();
   const int64_t row_elems = static_cast<int64_t>(a.n_q_heads) * head_dim;
   for (int s = lo; s < hi; ++s) {
     const int L = row_len(a, s);
@@ -171,33 +179,28 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
   if (tid >= 1 && tid <= 16) a.counters[tid] = 0;   // work-claim counters
 }
 
-// ------------------------------------------------------------------------------ MFMA path
+// ------------------------------------------------------------------------------ tile pipeline
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// PV on 16 tokens: O^T[16 dims][16 heads] += V^T[16 dims][16 tok] P^T[16 tok][16 heads]
-__device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, __bf16) {
-  s16x4 av, bv;
-  __builtin_memcpy(&av, &a, 8);
-  __builtin_memcpy(&bv, &b, 8);
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
-}
-__device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, _Float16) {
-  f16x4 av, bv;
-  __builtin_memcpy(&av, &a, 8);
-  __builtin_memcpy(&bv, &b, 8);
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
-}
+// Storage traits: X elements per 16-byte key vector; VV holds 4 consecutive tokens of one
+// value dimension.
+template <typename T> struct Kv;
+template <> struct Kv<__bf16> { static constexpr int X = 8; using VV = u32x2; };
+template <> struct Kv<_Float16> { static constexpr int X = 8; using VV = u32x2; };
+template <> struct Kv<float> { static constexpr int X = 4; using VV = u32x4; };
 
-// Register-resident tile of 16 tokens: the key rows in the A-operand layout of the QK
-// product (lane: token lane%16, 16-byte vectors 4ks+lane/16), the value columns in the
-// A-operand layout of the PV product (lane: dim 16dt+lane%16, tokens 4(lane/16)..+3).
-template <int D>
+// Register-resident tile of 16 tokens.  Keys: lane (token lane%16, group g = lane/16) holds
+// the 16-byte vectors 4ks+g of its token's row (the A operand of the MFMA QK product, and the
+// vector path's share of the dot product).  Values: lane (dim 16dt + lane%16, group g) holds
+// tokens 4g..4g+3 of that dim (the A operand of the MFMA PV product).
+template <typename T, int D>
 struct Tile16 {
-  u32x4 kf[D / 32];
-  u32x2 vf[D / 16];
+  static constexpr int NK = D / Kv<T>::X / 4;
+  u32x4 kf[NK];
+  typename Kv<T>::VV vf[D / 16];
 };
 
 // One work unit (row s, KV head kvh, partition part); all fields are wave-uniform.
@@ -226,24 +229,14 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   return u;
 }
 
-// q^T as the B operand of S^T = K q^T: lane (g, h) holds q[h][8*(4ks+g) .. +8].  Lanes of
-// padded heads (h >= G) read head 0 of the group: their columns are computed and discarded.
-template <typename T, int D>
-__device__ inline void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (&qr)[D / 32]) {
-  const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
-  const int h = r16 < a.group ? r16 : 0;
-  const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + h) * D;
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qr[ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * ks + g));
-}
-
 // Issues the loads of the 16-token tile at partition offset t0 of unit u.  Block ids are
 // wave-uniform scalar loads; table entries past the unit's last block are never read (those
 // tokens reuse the first id and are masked in the compute).
 template <typename T, int D, int Bsz>
 __device__ inline void issue_tile(const DecodeArgs& a, const Unit<T>& u, int t0, int64_t blk_stride,
-                                  Tile16<D>& R) {
-  constexpr int X = 8;
+                                  Tile16<T, D>& R) {
+  constexpr int X = Kv<T>::X;
+  using VV = typename Kv<T>::VV;
   constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
   const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int first = t0 / Bsz;
@@ -259,97 +252,272 @@ __device__ inline void issue_tile(const DecodeArgs& a, const Unit<T>& u, int t0,
   const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
   const T* kb = u.kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks)
     R.kf[ks] = *reinterpret_cast<const u32x4*>(kb + ks * 4 * Bsz * X);
   const int bv = (NB == 2 && g >= 2) ? id1 : id0;
   const T* vb = u.vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-    R.vf[dt] = *reinterpret_cast<const u32x2*>(vb + dt * 16 * Bsz);
+  for (int dt = 0; dt < D / 16; ++dt) R.vf[dt] = *reinterpret_cast<const VV*>(vb + dt * 16 * Bsz);
 }
 
-// QK^T, online softmax (base 2) and PV of one loaded 16-token tile.
+// q fragments of one query head hq of row s: lane (r16, g) holds the 16-byte vectors
+// 4ks+g of the head's row, matching the key fragments.
 template <typename T, int D>
-__device__ inline void compute_tile(const Tile16<D>& R, const u32x4 (*q_lds)[64], int t0, int ntok,
-                                    float scale_log2, float& m_run, float& l_run, f32x4 (&acc)[D / 16]) {
-  using V8 = typename Vec8<T>::type;
+__device__ inline void load_q_head(const DecodeArgs& a, int s, int hq, u32x4* qr) {
   const int g = threadIdx.x >> 4;
-  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(s) * a.n_q_heads + hq) * D;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const u32x4 qb = q_lds[ks][threadIdx.x];
-    V8 qv, kv;
-    __builtin_memcpy(&qv, &qb, 16);
-    __builtin_memcpy(&kv, &R.kf[ks], 16);
-    sc = mfma_16x16x32(kv, qv, sc);
+  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks)
+    qr[ks] = *reinterpret_cast<const u32x4*>(qrow + Kv<T>::X * (4 * ks + g));
+}
+
+// the X elements of a 16-byte vector as floats
+template <typename T>
+__device__ inline void unpack16(const u32x4& v, float* o) {
+  if constexpr (sizeof(T) == 4) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  } else {
+    T t[8];
+    __builtin_memcpy(t, &v, 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = to_f32(t[e]);
   }
-  // lane (g, h) holds the scores of tokens t0 + 4g + i, i = 0..3, for head h
-  float x[4];
+}
+template <typename T, typename VV>
+__device__ inline void unpack4(const VV& v, float* o) {
+  T t[4];
+  __builtin_memcpy(t, &v, 4 * sizeof(T));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = sc[i] * scale_log2;
-  const bool partial = t0 + 16 > ntok;
-  if (partial) {
+  for (int e = 0; e < 4; ++e) o[e] = to_f32(t[e]);
+}
+
+// ------------------------------------------------------------------------------ MFMA math
+// PV on 16 tokens: O^T[16 dims][16 heads] += V^T[16 dims][16 tok] P^T[16 tok][16 heads]
+__device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, __bf16) {
+  s16x4 av, bv;
+  __builtin_memcpy(&av, &a, 8);
+  __builtin_memcpy(&bv, &b, 8);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, _Float16) {
+  f16x4 av, bv;
+  __builtin_memcpy(&av, &a, 8);
+  __builtin_memcpy(&bv, &b, 8);
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
+}
+
+// G >= 3 query heads of one KV head on 16-bit KV: S^T = K q^T (16 tokens x 16 heads, G of
+// them real) and O^T += V^T P^T on MFMA.  The QK accumulator's lane layout (tokens 4g..4g+3
+// for head lane%16) is the PV B operand, so the weights never leave their lanes; they are
+// rounded to the KV type for the operand and the denominator sums the rounded values.
+template <typename T, int D>
+struct MfmaMath {
+  static constexpr int QH = 1;            // q fragment sets parked per unit
+  static constexpr bool kPrefetchQ = true;
+  using Tile = Tile16<T, D>;
+  f32x4 acc[D / 16];
+  float m_run, l_run;
+
+  __device__ void reset() {
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (t0 + 4 * g + i >= ntok) x[i] = -INFINITY;
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mt = fmaxf(mt, xor_f(mt, 16));
-  mt = fmaxf(mt, xor_f(mt, 32));
-  const float m_new = fmaxf(m_run, mt);
-  const float alpha = fast_exp2(m_run - m_new);
-  m_run = m_new;
-  T pt[4];
-  float psum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pt[i] = static_cast<T>(fast_exp2(x[i] - m_new));
-    psum += to_f32(pt[i]);
+  // lanes of padded heads (h >= G) read head 0 of the group: their columns are discarded
+  __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
+    const int r16 = threadIdx.x & 15;
+    load_q_head<T, D>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
   }
-  l_run = l_run * alpha + psum;
-  u32x2 pb;
-  __builtin_memcpy(&pb, pt, 8);
+  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
+    using V8 = typename Vec8<T>::type;
+    const int g = threadIdx.x >> 4;
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    u32x2 va = R.vf[dt];
+    for (int ks = 0; ks < Tile::NK; ++ks) {
+      const u32x4 qb = q_lds[0][ks][threadIdx.x];
+      V8 qv, kv;
+      __builtin_memcpy(&qv, &qb, 16);
+      __builtin_memcpy(&kv, &R.kf[ks], 16);
+      sc = mfma_16x16x32(kv, qv, sc);
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = sc[i] * scale_log2;
+    const bool partial = t0 + 16 > ntok;
     if (partial) {
-      T vt[4];
-      __builtin_memcpy(vt, &va, 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (t0 + 4 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
-      __builtin_memcpy(&va, vt, 8);
+        if (t0 + 4 * g + i >= ntok) x[i] = -INFINITY;
     }
-    acc[dt] = mfma_16x16x16(va, pb, acc[dt] * alpha, T{});
-  }
-}
-
-// Writes a finished unit: the normalised output when the row has one partition, else the
-// partition's (max, sum, unnormalised accumulator) for the merge kernel.
-template <typename T, int D>
-__device__ inline void finish_unit(const DecodeArgs& a, const Unit<T>& u, float m_run, float l_run,
-                                   const f32x4 (&acc)[D / 16]) {
-  const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
-  float l_tot = l_run + xor_f(l_run, 16);
-  l_tot += xor_f(l_tot, 32);
-  if (r16 >= a.group) return;
-  const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + r16;
-  if (u.nparts == 1) {
-    const float inv = 1.f / l_tot;
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, xor_f(mt, 16));
+    mt = fmaxf(mt, xor_f(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    T pt[4];
+    float psum = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) store4<T>(a.out, row * D + 16 * dt + 4 * g, acc[dt] * inv, a.out_f32);
-  } else {
-    const int64_t pidx = row * a.max_parts + u.part;
+    for (int i = 0; i < 4; ++i) {
+      pt[i] = static_cast<T>(fast_exp2(x[i] - m_new));
+      psum += to_f32(pt[i]);
+    }
+    l_run = l_run * alpha + psum;
+    u32x2 pb;
+    __builtin_memcpy(&pb, pt, 8);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<f32x4*>(a.part_acc + pidx * D + 16 * dt + 4 * g) = acc[dt];
-    if (g == 0) {
-      a.part_m[pidx] = m_run;
-      a.part_l[pidx] = l_tot;
+    for (int dt = 0; dt < D / 16; ++dt) {
+      u32x2 va = R.vf[dt];
+      if (partial) {
+        T vt[4];
+        __builtin_memcpy(vt, &va, 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
+        __builtin_memcpy(&va, vt, 8);
+      }
+      acc[dt] = mfma_16x16x16(va, pb, acc[dt] * alpha, T{});
     }
   }
-}
+  // the normalised output when the row has one partition, else (max, sum, accumulator)
+  __device__ void finish(const DecodeArgs& a, const Unit<T>& u) {
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    float l_tot = l_run + xor_f(l_run, 16);
+    l_tot += xor_f(l_tot, 32);
+    if (r16 >= a.group) return;
+    const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + r16;
+    if (u.nparts == 1) {
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) store4<T>(a.out, row * D + 16 * dt + 4 * g, acc[dt] * inv, a.out_f32);
+    } else {
+      const int64_t pidx = row * a.max_parts + u.part;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4*>(a.part_acc + pidx * D + 16 * dt + 4 * g) = acc[dt];
+      if (g == 0) {
+        a.part_m[pidx] = m_run;
+        a.part_l[pidx] = l_tot;
+      }
+    }
+  }
+};
 
+// ------------------------------------------------------------------------------ vector math
+// G <= 2 query heads on 16-bit KV, G <= 4 on fp32 KV (GM >= G): fp32 dot products per token (a lane's
+// 4ks+g vectors, then a 4-lane cross-group reduction), softmax over the tile's 16 tokens with
+// in-row reductions, fp32 weights, and FMA accumulation of the value columns (lane: dim
+// 16dt + lane%16 over tokens 4g..4g+3, summed over the 4 groups when the unit ends).
+template <typename T, int D, int GM>
+struct VecMath {
+  static constexpr int QH = GM;
+  static constexpr bool kPrefetchQ = GM == 1;   // more heads: q is loaded at the unit switch
+  using Tile = Tile16<T, D>;
+  static constexpr int X = Kv<T>::X;
+  float acc[GM][D / 16];
+  float m_run[GM], l_run[GM];
+  int group;
+
+  __device__ void reset() {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      m_run[gi] = -INFINITY;
+      l_run[gi] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[gi][dt] = 0.f;
+    }
+  }
+  __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) load_q_head<T, D>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
+  }
+  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const bool partial = t0 + 16 > ntok;
+    float kv[Tile::NK][X];
+#pragma unroll
+    for (int ks = 0; ks < Tile::NK; ++ks) unpack16<T>(R.kf[ks], kv[ks]);
+    float vv[D / 16][4];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      unpack4<T>(R.vf[dt], vv[dt]);
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * g + i >= ntok) vv[dt][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      if (gi >= group) break;
+      float dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < Tile::NK; ++ks) {
+        float qv[X];
+        unpack16<T>(q_lds[gi][ks][threadIdx.x], qv);
+#pragma unroll
+        for (int e = 0; e < X; ++e) dot = fmaf(qv[e], kv[ks][e], dot);
+      }
+      dot += xor_f(dot, 16);
+      dot += xor_f(dot, 32);
+      float xs = dot * scale_log2;
+      if (partial && t0 + r16 >= ntok) xs = -INFINITY;
+      float mt = fmaxf(xs, xor_f(xs, 1));
+      mt = fmaxf(mt, xor_f(mt, 2));
+      mt = fmaxf(mt, xor_f(mt, 4));
+      mt = fmaxf(mt, xor_f(mt, 8));
+      const float m_new = fmaxf(m_run[gi], mt);
+      const float alpha = fast_exp2(m_run[gi] - m_new);
+      m_run[gi] = m_new;
+      const float p = fast_exp2(xs - m_new);    // weight of token t0 + r16
+      l_run[gi] = l_run[gi] * alpha + (g == 0 ? p : 0.f);
+      float pe[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[i] = lane_fetch(p, 4 * g + i);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        float s4 = acc[gi][dt] * alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4 = fmaf(pe[i], vv[dt][i], s4);
+        acc[gi][dt] = s4;
+      }
+    }
+  }
+  __device__ void finish(const DecodeArgs& a, const Unit<T>& u) {
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      if (gi >= group) break;
+      float lt = l_run[gi];
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) lt += xor_f(lt, m);
+      float o[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        float v = acc[gi][dt] + xor_f(acc[gi][dt], 16);
+        o[dt] = v + xor_f(v, 32);
+      }
+      if (g != 0) continue;
+      const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + gi;
+      if (u.nparts == 1) {
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) store1<T>(a.out, row * D + 16 * dt + r16, o[dt] * inv, a.out_f32);
+      } else {
+        const int64_t pidx = row * a.max_parts + u.part;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) a.part_acc[pidx * D + 16 * dt + r16] = o[dt];
+        if (r16 == 0) {
+          a.part_m[pidx] = m_run[gi];
+          a.part_l[pidx] = lt;
+        }
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------ persistent kernel
 // A wave claims its next unit with one atomic on the work counter (lane 0); units are handed
 // out in plan order, largest first.
 __device__ inline int claim_unit(const DecodeArgs& a) {
@@ -360,60 +528,79 @@ __device__ inline int claim_unit(const DecodeArgs& a) {
 
 // Persistent wave over a stream of 16-token tiles of the units it claims, with the loads of
 // the tile two steps ahead in flight while the current tile is computed (three tile buffers
-// in rotation).  The issue side runs up to one unit ahead of the compute side; it loads that
-// unit's q into registers before the unit's first tile loads and parks it in the unit's LDS
-// slot one step later, after that step's tile loads are issued, so every wait in the steady
-// state covers exactly the tile about to be used.  When there is nothing left to issue it
-// re-issues the current tile's loads, so each step issues the same loads on every path.
-template <typename T, int D, int Bsz>
+// in rotation).  The issue side runs up to one unit ahead of the compute side.  With
+// kPrefetchQ it loads that unit's q into registers before the unit's first tile loads and
+// parks it in the unit's LDS slot one step later, after that step's tile loads are issued, so
+// every wait in the steady state covers exactly the tile about to be used; otherwise q is
+// loaded and parked when the compute side reaches the unit.  When there is nothing left to
+// issue it re-issues the current tile's loads (a filler the compute side skips), so each step
+// issues the same loads on every path.  The next unit is claimed a few tiles before it is
+// needed.
+template <typename T, int D, int Bsz, class Math>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_mfma_kernel(DecodeArgs a) {
+void decode_kernel(DecodeArgs a) {
+  using Tile = Tile16<T, D>;
+  constexpr int NK = Tile::NK;
   const int64_t chunk = static_cast<int64_t>(D) * Bsz;
   const int64_t blk_stride = chunk * a.n_kv_heads;
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
-  __shared__ u32x4 q_lds[2][D / 32][64];   // q fragments of the compute unit and the issue unit
+  __shared__ u32x4 q_lds[2][Math::QH][NK][64];   // q fragments: compute unit's and issue unit's
 
   const int first = __builtin_amdgcn_readfirstlane(claim_unit(a));
   if (first >= total) return;
   Unit<T> uc = open_unit<T>(a, first, chunk);   // compute cursor
   Unit<T> ui = uc;                              // issue cursor
-  u32x4 qr[D / 32];
-  load_q<T, D>(a, uc, qr);
+  u32x4 qr[Math::QH][NK];
+  Math::load_q(a, uc, qr);
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) q_lds[0][ks][threadIdx.x] = qr[ks];
+  for (int h = 0; h < Math::QH; ++h)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) q_lds[0][h][ks][threadIdx.x] = qr[h][ks];
   int slot_c = 0, slot_i = 0;
-  bool ahead = false;        // the issue cursor is in the unit after the compute cursor's
-  bool ended = false;        // no more units to claim
-  bool q_pending = false;    // qr holds the issue unit's q, not yet parked
+  // Wave-uniform state bits, packed in one word: separate flags captured by the lambdas below
+  // get their stores merged through a pointer select, which puts them in scratch.
+  constexpr unsigned kAhead = 1;    // the issue cursor is in the unit after the compute cursor's
+  constexpr unsigned kEnded = 2;    // no more units to claim
+  constexpr unsigned kQPend = 4;    // qr holds the issue unit's q, not yet parked
+  constexpr unsigned kClaimed = 8;  // `pending` holds a claim whose result is not read yet
+  unsigned fl = 0;
   int pending = 0;
-  bool claimed = false;      // `pending` holds a claim whose result is not read yet
   int ti = 0, tc = 0;
   constexpr int kClaimAhead = 4;   // claim the next unit this many tiles before it is needed
 
+  auto park_q = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < Math::QH; ++h)
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) q_lds[slot][h][ks][threadIdx.x] = qr[h][ks];
+  };
+
   // Fills Y with the next tile of the issue stream; returns false when Y only holds filler
   // loads (nothing real left to issue right now) that the compute side must skip.
-  auto issue_next = [&](Tile16<D>& Y) __attribute__((always_inline)) -> bool {
-    if (ti >= ui.ntok && !ahead && !ended) {
-      if (!claimed) pending = claim_unit(a);
+  auto issue_next = [&](Tile& Y) __attribute__((always_inline)) -> bool {
+    if (ti >= ui.ntok && !(fl & (kAhead | kEnded))) {
+      if (!(fl & kClaimed)) pending = claim_unit(a);
       const int un = __builtin_amdgcn_readfirstlane(pending);
-      claimed = false;
+      fl &= ~kClaimed;
       if (un < total) {
         ui = open_unit<T>(a, un, chunk);
         ti = 0;
-        ahead = true;
+        fl |= kAhead;
         slot_i = slot_c ^ 1;
-        load_q<T, D>(a, ui, qr);
-        q_pending = true;
+        if constexpr (Math::kPrefetchQ) {
+          Math::load_q(a, ui, qr);
+          fl |= kQPend;
+        }
       } else {
-        ended = true;
+        fl |= kEnded;
       }
     }
     if (ti < ui.ntok) {
       issue_tile<T, D, Bsz>(a, ui, ti, blk_stride, Y);
       ti += 16;
-      if (!claimed && !ended && ui.ntok - ti <= kClaimAhead * 16) {
+      if (!(fl & (kClaimed | kEnded)) && ui.ntok - ti <= kClaimAhead * 16) {
         pending = claim_unit(a);
-        claimed = true;
+        fl |= kClaimed;
       }
       return true;
     }
@@ -421,219 +608,52 @@ void decode_mfma_kernel(DecodeArgs a) {
     return false;
   };
 
-  Tile16<D> A, B, C;
-  bool rA = issue_next(A);
-  bool rB = issue_next(B);
-  bool rC = false;
+  Tile A, B, C;
+  // bit i set: buffer i (A, B, C) holds a real tile of the compute unit, clear: a filler
+  unsigned real = 0;
+  real |= issue_next(A) ? 1u : 0u;
+  real |= issue_next(B) ? 2u : 0u;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Math mt;
+  mt.reset();
+  if constexpr (!Math::kPrefetchQ) mt.group = a.group;
+  const float scale_log2 = a.scale_log2;
 
-  // X: the buffer issued two steps ago (rX: it holds a real tile of uc); Y gets the next issue.
-  auto step = [&](Tile16<D>& X, bool& rX, Tile16<D>& Y, bool& rY) __attribute__((always_inline)) -> bool {
-    if (q_pending) {   // loaded a step ago, before that step's tile loads
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) q_lds[slot_i][ks][threadIdx.x] = qr[ks];
-      q_pending = false;
+  // X: the buffer issued two steps ago; Y gets the next issue.  XI / YI are their bit positions.
+  auto step = [&](Tile& X, auto xi, Tile& Y, auto yi) __attribute__((always_inline)) -> bool {
+    constexpr unsigned XB = 1u << decltype(xi)::value, YB = 1u << decltype(yi)::value;
+    if constexpr (Math::kPrefetchQ) {
+      if (fl & kQPend) {   // loaded a step ago, before that step's tile loads
+        park_q(slot_i);
+        fl &= ~kQPend;
+      }
     }
-    rY = issue_next(Y);
-    if (!rX) return true;   // a filler: nothing to compute this step
-    compute_tile<T, D>(X, q_lds[slot_c], tc, uc.ntok, a.scale_log2, m_run, l_run, acc);
+    const bool x_real = (real & XB) != 0;
+    real = issue_next(Y) ? (real | YB) : (real & ~YB);
+    if (!x_real) return true;   // a filler: nothing to compute this step
+    mt.compute(X, q_lds[slot_c], tc, uc.ntok, scale_log2);
     tc += 16;
     if (tc < uc.ntok) return true;
-    finish_unit<T, D>(a, uc, m_run, l_run, acc);
-    if (!ahead) return false;   // the issue side found no further unit: every issued tile is filler
+    mt.finish(a, uc);
+    if (!(fl & kAhead)) return false;   // the issue side found no further unit: every issued tile is filler
     uc = ui;
     slot_c = slot_i;
-    ahead = false;
+    fl &= ~kAhead;
     tc = 0;
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mt.reset();
+    if constexpr (!Math::kPrefetchQ) {
+      Math::load_q(a, uc, qr);
+      park_q(slot_c);
+    }
     return true;
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   for (;;) {
-    if (!step(A, rA, C, rC)) break;
-    if (!step(B, rB, A, rA)) break;
-    if (!step(C, rC, B, rB)) break;
-  }
-}
-
-// ------------------------------------------------------------------------------ vector path
-template <typename T, int D, int GM>
-__global__ __launch_bounds__(64) void decode_vec_kernel(DecodeArgs a) {
-  constexpr int X = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte vector
-  constexpr int C = D / X;                              // vectors per key row
-  constexpr int KC = C / 4;                             // vectors per lane per token
-  constexpr int PPR = static_cast<int>(sizeof(T));      // 16-byte parts of a 16-token value row
-  constexpr int RSTEP = 64 / PPR;                       // rows covered per load instruction
-  constexpr int RPL = D / RSTEP;                        // value rows per lane
-  const int lane = threadIdx.x;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int vrow = lane / PPR;
-  const int vpart = lane % PPR;
-  const int Hk = a.n_kv_heads;
-  const int G = a.group;
-  const int Bsz = a.block_size;
-  const int lb = a.log2_block;
-  const int64_t chunk = static_cast<int64_t>(D) * Bsz;
-  const int64_t blk_stride = chunk * Hk;
-  const T* __restrict__ kpool = static_cast<const T*>(a.k_pool);
-  const T* __restrict__ vpool = static_cast<const T*>(a.v_pool);
-  const int total = a.counters[0] * Hk;
-
-  for (int u = next_unit(a, total); u >= 0; u = next_unit(a, total)) {
-    const int pair = u / Hk;
-    const int kvh = u - pair * Hk;
-    const int2 sp = a.units[pair];
-    const int s = sp.x;
-    const int part = sp.y;
-    const int L = row_len(a, s);
-    const int tok0 = part * a.part_tokens;
-    const int ntok = min(a.part_tokens, L - tok0);
-    const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.bt_stride + (tok0 >> lb);
-    const int nblk = (ntok + Bsz - 1) >> lb;
-    const T* kbase = kpool + static_cast<int64_t>(kvh) * chunk;
-    const T* vbase = vpool + static_cast<int64_t>(kvh) * chunk;
-
-    // q slices matching this lane's key vectors c = 4*kc + g
-    float qf[GM][KC][X];
-#pragma unroll
-    for (int gi = 0; gi < GM; ++gi) {
-      const T* qrow = static_cast<const T*>(a.q) +
-                      (static_cast<int64_t>(s) * a.n_q_heads + kvh * G + (gi < G ? gi : 0)) * D;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        T tmp[X];
-        const uint4 bits = *reinterpret_cast<const uint4*>(qrow + (4 * kc + g) * X);
-        __builtin_memcpy(tmp, &bits, 16);
-#pragma unroll
-        for (int e = 0; e < X; ++e) qf[gi][kc][e] = to_f32(tmp[e]);
-      }
-    }
-
-    float m_run[GM], l_part[GM], acc[RPL][GM];
-#pragma unroll
-    for (int gi = 0; gi < GM; ++gi) {
-      m_run[gi] = -INFINITY;
-      l_part[gi] = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < RPL; ++rr) acc[rr][gi] = 0.f;
-    }
-
-    for (int w0 = 0; w0 < nblk; w0 += 64) {
-      const int wb = min(64, nblk - w0);
-      int bid = lane < wb ? bt[w0 + lane] : 0;
-      bid = min(max(bid, 0), a.num_blocks - 1);
-      const int wend = min(ntok, (w0 + 64) << lb);
-      for (int t0 = w0 << lb; t0 < wend; t0 += 16) {
-        // keys: lane (token r16, column group g)
-        const int j = t0 + r16;
-        uint4 kf[KC];
-        {
-          const int b = lane_fetch(bid, (j >> lb) - w0);
-          const T* kb = kbase + static_cast<int64_t>(b) * blk_stride + (j & (Bsz - 1)) * X;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            kf[kc] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(4 * kc + g) * Bsz * X);
-        }
-        // values: lane (row vrow + RSTEP*rr, tokens t0 + vpart*X .. +X-1)
-        uint4 vv[RPL];
-        const int jv = t0 + vpart * X;
-        {
-          const int b = lane_fetch(bid, (jv >> lb) - w0);
-          const T* vb = vbase + static_cast<int64_t>(b) * blk_stride + (jv & (Bsz - 1));
-#pragma unroll
-          for (int rr = 0; rr < RPL; ++rr)
-            vv[rr] = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(vrow + RSTEP * rr) * Bsz);
-        }
-        const bool partial = t0 + 16 > ntok;
-        float p[GM];
-#pragma unroll
-        for (int gi = 0; gi < GM; ++gi) {
-          float dot = 0.f;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            T tmp[X];
-            __builtin_memcpy(tmp, &kf[kc], 16);
-#pragma unroll
-            for (int e = 0; e < X; ++e) dot = fmaf(qf[gi][kc][e], to_f32(tmp[e]), dot);
-          }
-          dot += xor_f(dot, 16);
-          dot += xor_f(dot, 32);
-          float xs = dot * a.scale_log2;
-          if (partial && j >= ntok) xs = -INFINITY;
-          float mt = xs;
-          mt = fmaxf(mt, xor_f(mt, 1));
-          mt = fmaxf(mt, xor_f(mt, 2));
-          mt = fmaxf(mt, xor_f(mt, 4));
-          mt = fmaxf(mt, xor_f(mt, 8));
-          const float m_new = fmaxf(m_run[gi], mt);
-          const float alpha = fast_exp2(m_run[gi] - m_new);
-          m_run[gi] = m_new;
-          p[gi] = fast_exp2(xs - m_new);
-          l_part[gi] = l_part[gi] * alpha + (g == 0 ? p[gi] : 0.f);
-#pragma unroll
-          for (int rr = 0; rr < RPL; ++rr) acc[rr][gi] *= alpha;
-        }
-        // weighted values
-#pragma unroll
-        for (int e = 0; e < X; ++e) {
-          const bool tok_ok = !partial || (jv + e < ntok);
-          float pe[GM];
-#pragma unroll
-          for (int gi = 0; gi < GM; ++gi) pe[gi] = lane_fetch(p[gi], vpart * X + e);
-#pragma unroll
-          for (int rr = 0; rr < RPL; ++rr) {
-            T tmp[X];
-            __builtin_memcpy(tmp, &vv[rr], 16);
-            const float vval = tok_ok ? to_f32(tmp[e]) : 0.f;
-#pragma unroll
-            for (int gi = 0; gi < GM; ++gi) acc[rr][gi] = fmaf(pe[gi], vval, acc[rr][gi]);
-          }
-        }
-      }
-    }
-
-    // ---- finish
-#pragma unroll
-    for (int gi = 0; gi < GM; ++gi) {
-      float lt = l_part[gi];
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) lt += xor_f(lt, m);
-      l_part[gi] = lt;
-#pragma unroll
-      for (int rr = 0; rr < RPL; ++rr) {
-#pragma unroll
-        for (int m = 1; m < PPR; m <<= 1) acc[rr][gi] += xor_f(acc[rr][gi], m);
-      }
-    }
-    if (vpart == 0) {
-#pragma unroll
-      for (int gi = 0; gi < GM; ++gi) {
-        if (gi >= G) break;
-        const int64_t row = static_cast<int64_t>(s) * a.n_q_heads + kvh * G + gi;
-        if (nparts == 1) {
-          const float inv = 1.f / l_part[gi];
-#pragma unroll
-          for (int rr = 0; rr < RPL; ++rr)
-            store1<T>(a.out, row * D + vrow + RSTEP * rr, acc[rr][gi] * inv, a.out_f32);
-        } else {
-          const int64_t pidx = row * a.max_parts + part;
-#pragma unroll
-          for (int rr = 0; rr < RPL; ++rr) a.part_acc[pidx * D + vrow + RSTEP * rr] = acc[rr][gi];
-          if (lane == 0) {
-            a.part_m[pidx] = m_run[gi];
-            a.part_l[pidx] = l_part[gi];
-          }
-        }
-      }
-    }
+    if (!step(A, I0{}, C, I2{})) break;
+    if (!step(B, I1{}, A, I0{})) break;
+    if (!step(C, I2{}, B, I1{})) break;
   }
 }
 
@@ -702,54 +722,33 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename T, int D>
-const void* mfma_kernel_ptr_d(int block_size) {
+template <typename T, int D, class Math>
+const void* kernel_ptr_b(int block_size) {
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_mfma_kernel<T, D, 8>);
-    case 16: return reinterpret_cast<const void*>(&decode_mfma_kernel<T, D, 16>);
-    case 32: return reinterpret_cast<const void*>(&decode_mfma_kernel<T, D, 32>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<T, D, 8, Math>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<T, D, 16, Math>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<T, D, 32, Math>);
     default: return nullptr;
   }
 }
-template <typename T>
-const void* mfma_kernel_ptr(int head_dim, int block_size) {
-  return head_dim == 128 ? mfma_kernel_ptr_d<T, 128>(block_size) : mfma_kernel_ptr_d<T, 64>(block_size);
-}
 
-template <typename T>
-hipError_t main_dispatch(const DecodeArgs& a, int head_dim, int path, int32_t grid, hipStream_t st) {
-  const dim3 blk(64), grd(grid);
+template <typename T, int D>
+const void* kernel_ptr_d(int path, int group, int block_size) {
   if (path == 1) {
-    if constexpr (sizeof(T) == 2) {
-      const void* fn = mfma_kernel_ptr<T>(head_dim, a.block_size);
-      if (!fn) return hipErrorInvalidValue;
-      void* args[] = {const_cast<DecodeArgs*>(&a)};
-      return hipLaunchKernel(fn, grd, blk, args, 0, st);
-    }
-    return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2) return kernel_ptr_b<T, D, MfmaMath<T, D>>(block_size);
+    return nullptr;
   }
-  const bool one = a.group == 1;
-  if (head_dim == 128) {
-    if (one) decode_vec_kernel<T, 128, 1><<<grd, blk, 0, st>>>(a);
-    else decode_vec_kernel<T, 128, 4><<<grd, blk, 0, st>>>(a);
-  } else {
-    if (one) decode_vec_kernel<T, 64, 1><<<grd, blk, 0, st>>>(a);
-    else decode_vec_kernel<T, 64, 4><<<grd, blk, 0, st>>>(a);
-  }
-  return hipGetLastError();
+  if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>>(block_size);
+  if (group == 2) return kernel_ptr_b<T, D, VecMath<T, D, 2>>(block_size);
+  // 16-bit KV with three or more heads per group takes the MFMA path
+  if constexpr (sizeof(T) == 4) return kernel_ptr_b<T, D, VecMath<T, D, 4>>(block_size);
+  return nullptr;
 }
 
 template <typename T>
 const void* main_kernel_ptr(int head_dim, int path, int group, int block_size) {
-  if (path == 1) {
-    if constexpr (sizeof(T) == 2) return mfma_kernel_ptr<T>(head_dim, block_size);
-    return nullptr;
-  }
-  if (head_dim == 128)
-    return group == 1 ? reinterpret_cast<const void*>(&decode_vec_kernel<T, 128, 1>)
-                      : reinterpret_cast<const void*>(&decode_vec_kernel<T, 128, 4>);
-  return group == 1 ? reinterpret_cast<const void*>(&decode_vec_kernel<T, 64, 1>)
-                    : reinterpret_cast<const void*>(&decode_vec_kernel<T, 64, 4>);
+  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size)
+                         : kernel_ptr_d<T, 64>(path, group, block_size);
 }
 
 }  // namespace
@@ -763,9 +762,12 @@ hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipS
 
 hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, int32_t grid,
                               hipStream_t st) {
-  if (dtype == PKV_F32) return main_dispatch<float>(a, head_dim, path, grid, st);
-  if (dtype == PKV_F16) return main_dispatch<_Float16>(a, head_dim, path, grid, st);
-  return main_dispatch<__bf16>(a, head_dim, path, grid, st);
+  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size)
+                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size)
+                                      : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(fn, dim3(grid), dim3(64), args, 0, st);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
