@@ -56,6 +56,11 @@ def parse():
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                   help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
+                        "--copy-calibration into the traffic record (CPU only; writes --pmc-out)")
+    p.add_argument("--pmc-out", default=os.path.join(ROOT, "profiles", "decode_traffic_llama70b_gqa.json"))
+    p.add_argument("--pmc-command", default="", help="the command lines that produced the CSVs (recorded)")
     return p.parse_args()
 
 
@@ -138,17 +143,129 @@ def time_steps(w, steps, warmup, decode_only=False):
             "lens0": lens0}
 
 
-def roofline(res):
+# Sources whose change invalidates measured HBM counters of the decode kernel.
+KERNEL_SOURCES = ("paged_kv_cache_53_amd/csrc/decode.hip", "paged_kv_cache_53_amd/csrc/api.hip",
+                  "paged_kv_cache_53_amd/csrc/pkv_internal.h")
+DECODE_KERNEL_PREFIX = "_ZN3pkv12_GLOBAL__N_113decode_kernel"
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def workload_key(w):
+    return {"workload": w.name, "variant": w.variant, "block_size": w.block_size,
+            "partition_size": w.partition_size, "placement": w.placement}
+
+
+def measured_traffic(w):
+    """HBM bytes per decode launch from the committed counter record, or None when the record
+    was taken on other kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic_llama70b_gqa.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256() or rec.get("workload") != workload_key(w):
+        return None
+    return rec
+
+
+def roofline(res, w=None, decode_only=False):
     n_dec, ms_dec = res["kernels"].get("decode", (0, 0.0))
     if not n_dec:
         return None
     per_launch = (res["kv_bytes"] + res["table_bytes"]) / res["steps"]
     avg_s = ms_dec / n_dec / 1e3
     achieved = per_launch / avg_s / 1e9
-    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-            "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV with G >= 3)",
-            "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
+    rec = measured_traffic(w) if w is not None else None
+    out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBPS, 4),
+           # measured HBM bytes per launch: the counters' bytes-per-algorithmic-byte ratio of this
+           # kernel on this workload, times this run's algorithmic bytes per launch
+           "traffic": int(rec["traffic_over_algorithmic"] * per_launch) if rec else None,
+           "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV with G >= 3)",
+           "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
+    if rec:
+        out["traffic_detail"] = {"fetch_bytes": int(rec["fetch_over_algorithmic"] * per_launch),
+                                 "write_bytes": int(rec["write_over_algorithmic"] * per_launch),
+                                 "source": "profiles/decode_traffic_llama70b_gqa.json"}
+    return out
+
+
+# ------------------------------------------------------------------------------------- counters
+def _pmc_rows(path, counter):
+    import csv
+    with open(path, newline="") as f:
+        rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return rows
+
+
+def pmc_summary(args):
+    """Calibrated HBM traffic of the decode kernel from FETCH_SIZE / WRITE_SIZE counter CSVs.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by what it reads for a
+    plain copy of known size (the 1 GiB copy kernel of --copy-calibration reads and writes 1 GiB).
+    """
+    import statistics
+    fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.pmc_summary
+    copy_kib = (1 << 30) / 1024.0
+
+    def copy_reading(path, counter):
+        rows = [r for r in _pmc_rows(path, counter) if "copyBuffer" in r["Kernel_Name"]]
+        if not rows:
+            raise SystemExit(f"no copy kernel rows for {counter} in {path}")
+        return statistics.median(float(r["Counter_Value"]) for r in rows)
+
+    def decode_readings(path, counter):
+        rows = [r for r in _pmc_rows(path, counter) if r["Kernel_Name"].startswith(DECODE_KERNEL_PREFIX)]
+        if not rows:
+            raise SystemExit(f"no decode kernel rows for {counter} in {path}")
+        return [float(r["Counter_Value"]) for r in rows], rows[0]["Kernel_Name"]
+
+    f_scale = copy_kib / copy_reading(cal_fetch_csv, "FETCH_SIZE")
+    w_scale = copy_kib / copy_reading(cal_write_csv, "WRITE_SIZE")
+    f_vals, kname = decode_readings(fetch_csv, "FETCH_SIZE")
+    w_vals, _ = decode_readings(write_csv, "WRITE_SIZE")
+    import numpy as np
+
+    import workloads as wl
+    w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
+                 copied_prefix=args.copied_prefix, partition_size=args.partition_size)
+    # decode dispatch j of the profiled bench run attends over the prompt (L - 1 tokens) plus the
+    # j + 1 tokens appended so far; a --decode-only run appends nothing
+    prompt = w.seq_lens.astype(np.int64) - 1
+
+    def algo(j):
+        kvb, tb = kv_bytes(w, prompt if args.decode_only else prompt + j + 1)
+        return kvb + tb
+
+    f_ratio = statistics.median(v * f_scale * 1024 / algo(j) for j, v in enumerate(f_vals))
+    w_ratio = statistics.median(v * w_scale * 1024 / algo(j) for j, v in enumerate(w_vals))
+    a_last = algo(len(f_vals) - 1)
+    rec = {
+        "kernel": kname, "workload": workload_key(w), "kernel_sources_sha256": kernel_sources_sha256(),
+        "profiled_run": {"steps": args.steps, "warmup": args.warmup, "decode_only": bool(args.decode_only),
+                         "decode_launches": {"fetch": len(f_vals), "write": len(w_vals)}},
+        "raw_kib_per_launch_median": {"FETCH_SIZE": statistics.median(f_vals),
+                                      "WRITE_SIZE": statistics.median(w_vals)},
+        "calibration": {"copy_bytes": 1 << 30, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "fetch_over_algorithmic": round(f_ratio, 5), "write_over_algorithmic": round(w_ratio, 5),
+        "traffic_over_algorithmic": round(f_ratio + w_ratio, 5),
+        "last_launch": {"algorithmic_bytes": int(a_last), "fetch_bytes": int(f_vals[-1] * f_scale * 1024),
+                        "write_bytes": int(w_vals[-1] * w_scale * 1024)},
+        "command": args.pmc_command,
+    }
+    os.makedirs(os.path.dirname(args.pmc_out), exist_ok=True)
+    with open(args.pmc_out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
 
 
 # ------------------------------------------------------------------------------------- CPU oracle
@@ -209,6 +326,8 @@ def _oracle_sample(w, budget_s, cores, used):
 # ------------------------------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.pmc_summary:
+        return pmc_summary(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by sequence "
               "or KV head with no exchange, but this build measures the one-GPU share", file=sys.stderr)
@@ -252,7 +371,7 @@ def main():
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(seqs_s, 1),
         "kernels": kern,
-        "roofline": roofline(res),
+        "roofline": roofline(res, w),
     }
     if args.config == 4:
         # unique bytes: the shared prompt is stored (and mostly fetched from HBM) once
