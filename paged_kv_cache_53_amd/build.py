@@ -3,7 +3,9 @@
 HIP sources go through hipcc for gfx950 with packed-FP32 instruction
 selection switched off (-Xclang -target-feature -Xclang -packed-fp32-ops);
 the host allocator is plain C++17 and goes through g++.  Objects land in
-``_build/`` next to this file, the shared library next to this file.
+``_build/`` next to this file, the shared library next to this file.  The decode kernels' device
+assembly is checked for the discipline their explicitly waited loads rely on
+(``verify_waits``); the build fails if it does not hold.
 
 Usage: python -m paged_kv_cache_53_amd.build [-v]
 """
@@ -24,6 +26,10 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_SOURCES = ["api.hip", "scatter.hip", "decode.hip"]
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # keep a wave's work-claim atomic as written: the optimiser's rewrite reads the result
+             # at once, making the wave wait for all of its outstanding loads
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 CXX_SOURCES = ["allocator.cpp"]
 
 
@@ -52,19 +58,25 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([hipcc, f"--offload-arch={ARCH}", *common,
-                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                     # keep a wave's work-claim atomic as written: the optimiser's rewrite reads the
-                     # result at once, making the wave wait for all of its outstanding loads
-                     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+        cmds.append([hipcc, f"--offload-arch={ARCH}", *common, *HIP_FLAGS,
                      "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         cmds.append(["g++", *common, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # device assembly of the decode kernels, for the static check of their explicit waits
+    asm = os.path.join(BUILD, "decode.s")
+    cmds.append([hipcc, f"--offload-arch={ARCH}", *common, *HIP_FLAGS, "-S", "--cuda-device-only",
+                 os.path.join(CSRC, "decode.hip"), "-o", asm])
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
+    from .verify_waits import check_file
+    bad = {k: v for k, v in check_file(asm).items() if v}
+    if bad:
+        lines = [f"{k}:\n    " + "\n    ".join(v[:10]) for k, v in bad.items()]
+        raise RuntimeError("decode kernels touch registers of in-flight explicitly waited loads:\n" +
+                           "\n".join(lines))
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -185,6 +185,39 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
+// Explicitly waited vector-memory operations.  The tile stream's loads, the early q loads and
+// the work-claim atomic are issued through inline assembly, which the compiler's wait
+// insertion does not track; across the pipeline's branches its merged bookkeeping otherwise
+// drains every outstanding load before each new tile is issued.  Each operation names its
+// destination as an in/out operand, so those registers stay with their buffer for the whole
+// loop and are never reused as temporaries, and every use of the loaded data comes after an
+// explicit "s_waitcnt vmcnt(N)" followed by tie() on the same registers, where N is a count of
+// vector-memory instructions the pipeline always issues after the operation.  vmcnt counts
+// loads, stores and atomics together and they retire in order, so waiting for at most N
+// outstanding, with N no larger than the number issued since, guarantees completion.
+// The loads carry the non-temporal hint: the key and value stream is read once per call, and
+// keeping it from displacing other lines in L2 and the Infinity Cache measured 5 % faster (the
+// partial results the merge kernel reads next stay resident).
+// With E false (tiles too large to keep three in registers without spilling, where a spill of
+// an in-flight register would be wrong) every helper is the ordinary compiler-tracked form.
+template <bool E>
+__device__ inline void vload(u32x4& d, const void* p) {
+  if constexpr (E) asm volatile("global_load_dwordx4 %0, %1, off nt" : "+v"(d) : "v"(p));
+  else d = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+template <bool E>
+__device__ inline void vload(u32x2& d, const void* p) {
+  if constexpr (E) asm volatile("global_load_dwordx2 %0, %1, off nt" : "+v"(d) : "v"(p));
+  else d = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+}
+// waits until at most N vector-memory operations are outstanding
+template <bool E, int N> __device__ inline void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  if constexpr (E) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N));
+}
+// orders every later use of r after the preceding wait
+template <bool E, typename R> __device__ inline void tie(R& r) { if constexpr (E) asm volatile("" : "+v"(r)); }
+
 // Storage traits: X elements per 16-byte key vector; VV holds 4 consecutive tokens of one
 // value dimension.
 template <typename T> struct Kv;
@@ -199,6 +232,7 @@ template <> struct Kv<float> { static constexpr int X = 4; using VV = u32x4; };
 template <typename T, int D>
 struct Tile16 {
   static constexpr int NK = D / Kv<T>::X / 4;
+  static constexpr int kLoads = NK + D / 16;   // vector-memory instructions per tile
   u32x4 kf[NK];
   typename Kv<T>::VV vf[D / 16];
 };
@@ -229,46 +263,49 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   return u;
 }
 
-// Issues the loads of the 16-token tile at partition offset t0 of unit u.  Block ids are
+// Issues the Tile16::kLoads loads of the 16-token tile at partition offset t0 of a unit (block
+// table row bt, ntok tokens, pools offset to its KV head), completion explicitly waited when E
+// (vload).  Block ids are
 // wave-uniform scalar loads; table entries past the unit's last block are never read (those
 // tokens reuse the first id and are masked in the compute).
-template <typename T, int D, int Bsz>
-__device__ inline void issue_tile(const DecodeArgs& a, const Unit<T>& u, int t0, int64_t blk_stride,
-                                  Tile16<T, D>& R) {
+template <typename T, int D, int Bsz, bool E>
+__device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int ntok, const T* kbase,
+                                  const T* vbase, int t0, int64_t blk_stride, Tile16<T, D>& R) {
   constexpr int X = Kv<T>::X;
   using VV = typename Kv<T>::VV;
   constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
   const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int first = t0 / Bsz;
-  int id0 = ld_uniform(u.bt, first);
+  int id0 = ld_uniform(bt, first);
   id0 = min(max(id0, 0), a.num_blocks - 1);
   int id1 = id0;
   if constexpr (NB == 2) {
-    if (t0 + 8 < u.ntok) {
-      id1 = ld_uniform(u.bt, first + 1);
+    if (t0 + 8 < ntok) {
+      id1 = ld_uniform(bt, first + 1);
       id1 = min(max(id1, 0), a.num_blocks - 1);
     }
   }
   const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
-  const T* kb = u.kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
+  const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
 #pragma unroll
-  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks)
-    R.kf[ks] = *reinterpret_cast<const u32x4*>(kb + ks * 4 * Bsz * X);
+  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) vload<E>(R.kf[ks], kb + ks * 4 * Bsz * X);
   const int bv = (NB == 2 && g >= 2) ? id1 : id0;
-  const T* vb = u.vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
+  const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) R.vf[dt] = *reinterpret_cast<const VV*>(vb + dt * 16 * Bsz);
+  for (int dt = 0; dt < D / 16; ++dt) vload<E>(R.vf[dt], vb + dt * 16 * Bsz);
 }
 
 // q fragments of one query head hq of row s: lane (r16, g) holds the 16-byte vectors
 // 4ks+g of the head's row, matching the key fragments.
-template <typename T, int D>
+// kAsync: issued with vload (the caller waits explicitly); otherwise ordinary loads.
+template <typename T, int D, bool kAsync>
 __device__ inline void load_q_head(const DecodeArgs& a, int s, int hq, u32x4* qr) {
   const int g = threadIdx.x >> 4;
   const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(s) * a.n_q_heads + hq) * D;
 #pragma unroll
-  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks)
-    qr[ks] = *reinterpret_cast<const u32x4*>(qrow + Kv<T>::X * (4 * ks + g));
+  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) {
+    vload<kAsync>(qr[ks], qrow + Kv<T>::X * (4 * ks + g));
+  }
 }
 
 // the X elements of a 16-byte vector as floats
@@ -325,9 +362,10 @@ struct MfmaMath {
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // lanes of padded heads (h >= G) read head 0 of the group: their columns are discarded
+  template <bool kAsync>
   __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
     const int r16 = threadIdx.x & 15;
-    load_q_head<T, D>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
+    load_q_head<T, D, kAsync>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
   }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
     using V8 = typename Vec8<T>::type;
@@ -428,9 +466,11 @@ struct VecMath {
       for (int dt = 0; dt < D / 16; ++dt) acc[gi][dt] = 0.f;
     }
   }
+  template <bool kAsync>
   __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
 #pragma unroll
-    for (int gi = 0; gi < GM; ++gi) load_q_head<T, D>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
+    for (int gi = 0; gi < GM; ++gi)
+      load_q_head<T, D, kAsync>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
   }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
@@ -518,12 +558,28 @@ struct VecMath {
 };
 
 // ------------------------------------------------------------------------------ persistent kernel
-// A wave claims its next unit with one atomic on the work counter (lane 0); units are handed
-// out in plan order, largest first.
-__device__ inline int claim_unit(const DecodeArgs& a) {
-  int u = 0;
-  if (threadIdx.x == 0) u = atomicAdd(&a.counters[1], 1);
-  return u;  // valid in lane 0 only; read with readfirstlane when needed
+// A wave claims its next unit with one atomic on the work counter; units are handed out in
+// plan order, largest first.  Lane 0 alone executes the atomic: exec is narrowed inside the
+// asm, so the result never passes through a divergent-branch merge that the compiler could
+// copy before the value arrives.  The previous index in `slot` (lane 0) is valid once a wait
+// covers the atomic; read it with readfirstlane.  Called with all lanes active (uniform
+// control flow).
+template <bool E>
+__device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
+  if constexpr (!E) {
+    int u = 0;
+    if (threadIdx.x == 0) u = atomicAdd(&a.counters[1], 1);
+    slot = u;
+    return;
+  }
+  unsigned long long saved;
+  asm volatile(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %0, %2, %3, off sc0\n\t"
+      "s_mov_b64 exec, %1"
+      : "+v"(slot), "=&s"(saved)
+      : "v"(a.counters + 1), "v"(1));
 }
 
 // Persistent wave over a stream of 16-token tiles of the units it claims, with the loads of
@@ -541,17 +597,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
   using Tile = Tile16<T, D>;
   constexpr int NK = Tile::NK;
+  // explicitly waited loads while three tiles fit in 96 registers (32 per tile)
+  constexpr bool E = sizeof(Tile) <= 32 * 4;
+  constexpr int LT = Tile::kLoads;   // every step issues exactly this many tile loads
   const int64_t chunk = static_cast<int64_t>(D) * Bsz;
   const int64_t blk_stride = chunk * a.n_kv_heads;
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
   __shared__ u32x4 q_lds[2][Math::QH][NK][64];   // q fragments: compute unit's and issue unit's
 
-  const int first = __builtin_amdgcn_readfirstlane(claim_unit(a));
+  int pending = 0;
+  claim_unit<E>(a, pending);
+  vm_wait<E, 0>();
+  tie<E>(pending);
+  const int first = __builtin_amdgcn_readfirstlane(pending);
   if (first >= total) return;
   Unit<T> uc = open_unit<T>(a, first, chunk);   // compute cursor
   Unit<T> ui = uc;                              // issue cursor
   u32x4 qr[Math::QH][NK];
-  Math::load_q(a, uc, qr);
+  Math::template load_q<false>(a, uc, qr);
 #pragma unroll
   for (int h = 0; h < Math::QH; ++h)
 #pragma unroll
@@ -564,7 +627,6 @@ void decode_kernel(DecodeArgs a) {
   constexpr unsigned kQPend = 4;    // qr holds the issue unit's q, not yet parked
   constexpr unsigned kClaimed = 8;  // `pending` holds a claim whose result is not read yet
   unsigned fl = 0;
-  int pending = 0;
   int ti = 0, tc = 0;
   constexpr int kClaimAhead = 4;   // claim the next unit this many tiles before it is needed
 
@@ -577,42 +639,55 @@ void decode_kernel(DecodeArgs a) {
 
   // Fills Y with the next tile of the issue stream; returns false when Y only holds filler
   // loads (nothing real left to issue right now) that the compute side must skip.
-  auto issue_next = [&](Tile& Y) __attribute__((always_inline)) -> bool {
+  // tc_now: the compute cursor's tile offset, passed by value (a reference capture keeps tc in memory)
+  auto issue_next = [&](Tile& Y, int tc_now) __attribute__((always_inline)) -> bool {
     if (ti >= ui.ntok && !(fl & (kAhead | kEnded))) {
-      if (!(fl & kClaimed)) pending = claim_unit(a);
+      // A claim made by an earlier step preceded that step's LT tile loads: at most LT
+      // outstanding means it has returned.  Without one, claim now and drain.
+      if (!(fl & kClaimed)) {
+        claim_unit<E>(a, pending);
+        vm_wait<E, 0>();
+      }
+      vm_wait<E, LT>();   // on both paths, so the wait does not hang on a branch condition
+      tie<E>(pending);
       const int un = __builtin_amdgcn_readfirstlane(pending);
       fl &= ~kClaimed;
-      if (un < total) {
+      if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
         ui = open_unit<T>(a, un, chunk);
         ti = 0;
         fl |= kAhead;
         slot_i = slot_c ^ 1;
         if constexpr (Math::kPrefetchQ) {
-          Math::load_q(a, ui, qr);
+          Math::template load_q<E>(a, ui, qr);
           fl |= kQPend;
         }
       } else {
         fl |= kEnded;
       }
     }
-    if (ti < ui.ntok) {
-      issue_tile<T, D, Bsz>(a, ui, ti, blk_stride, Y);
-      ti += 16;
-      if (!(fl & (kClaimed | kEnded)) && ui.ntok - ti <= kClaimAhead * 16) {
-        pending = claim_unit(a);
-        fl |= kClaimed;
-      }
-      return true;
+    const bool is_real = ti < ui.ntok;
+    // the claim goes before this step's tile loads, so they count towards its wait
+    if (is_real && !(fl & (kClaimed | kEnded)) && ui.ntok - (ti + 16) <= kClaimAhead * 16) {
+      claim_unit<E>(a, pending);
+      fl |= kClaimed;
     }
-    issue_tile<T, D, Bsz>(a, uc, tc, blk_stride, Y);   // filler: keeps the per-step loads uniform
-    return false;
+    // One load sequence on every path (a filler re-reads the compute cursor's tile, which keeps
+    // the per-step loads uniform): separate sequences would meet in a merge that the compiler
+    // may resolve by copying the loaded registers before the data arrives.
+    // (unary + makes each operand a value: a select of lvalues selects their addresses, which
+    // keeps the variables out of registers)
+    issue_tile<T, D, Bsz, E>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.ntok : +uc.ntok,
+                             is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
+                             is_real ? +ti : tc_now, blk_stride, Y);
+    ti += is_real ? 16 : 0;   // a select: a conditional update would put ti in memory
+    return is_real;
   };
 
-  Tile A, B, C;
+  Tile A{}, B{}, C{};   // defined before their first load, which names them as in/out operands
   // bit i set: buffer i (A, B, C) holds a real tile of the compute unit, clear: a filler
   unsigned real = 0;
-  real |= issue_next(A) ? 1u : 0u;
-  real |= issue_next(B) ? 2u : 0u;
+  real |= issue_next(A, 0) ? 1u : 0u;
+  real |= issue_next(B, 0) ? 2u : 0u;
 
   Math mt;
   mt.reset();
@@ -623,13 +698,24 @@ void decode_kernel(DecodeArgs a) {
   auto step = [&](Tile& X, auto xi, Tile& Y, auto yi) __attribute__((always_inline)) -> bool {
     constexpr unsigned XB = 1u << decltype(xi)::value, YB = 1u << decltype(yi)::value;
     if constexpr (Math::kPrefetchQ) {
-      if (fl & kQPend) {   // loaded a step ago, before that step's tile loads
+      if (fl & kQPend) {   // loaded a step ago, before that step's LT tile loads
+        vm_wait<E, LT>();
+#pragma unroll
+        for (int h = 0; h < Math::QH; ++h)
+#pragma unroll
+          for (int ks = 0; ks < NK; ++ks) tie<E>(qr[h][ks]);
         park_q(slot_i);
         fl &= ~kQPend;
       }
     }
     const bool x_real = (real & XB) != 0;
-    real = issue_next(Y) ? (real | YB) : (real & ~YB);
+    real = issue_next(Y, tc) ? (real | YB) : (real & ~YB);
+    // X was issued two steps ago; each of the two steps since issued LT tile loads
+    vm_wait<E, 2 * LT>();
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) tie<E>(X.kf[ks]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) tie<E>(X.vf[dt]);
     if (!x_real) return true;   // a filler: nothing to compute this step
     mt.compute(X, q_lds[slot_c], tc, uc.ntok, scale_log2);
     tc += 16;
@@ -642,7 +728,7 @@ void decode_kernel(DecodeArgs a) {
     tc = 0;
     mt.reset();
     if constexpr (!Math::kPrefetchQ) {
-      Math::load_q(a, uc, qr);
+      Math::template load_q<false>(a, uc, qr);   // the compiler waits for these itself
       park_q(slot_c);
     }
     return true;
@@ -655,6 +741,7 @@ void decode_kernel(DecodeArgs a) {
     if (!step(B, I1{}, A, I0{})) break;
     if (!step(C, I2{}, B, I1{})) break;
   }
+  vm_wait<E, 0>();   // filler loads still in flight land before the wave ends
 }
 
 // ------------------------------------------------------------------------------ merge
