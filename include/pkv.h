@@ -253,6 +253,10 @@ typedef struct {
 
 int pkv_timing_enable(int enable);
 int pkv_timing_collect(pkv_kernel_time* out, int32_t cap, int32_t* n);
+/* Restricts timing to the kernel ids whose bit (1u << id) is set in mask (default: all).
+ * Each timed launch adds an event pair to its stream, so timing only the kernel of interest
+ * keeps that overhead out of a timed region.  Forgets pending records. */
+int pkv_timing_select(uint32_t mask);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PK
 __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
-    "timing_enable", "timing_collect", "lib",
+    "timing_enable", "timing_select", "timing_collect", "lib",
 ]
 
 
@@ -145,6 +145,18 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
 
 def timing_enable(on: bool = True) -> None:
     _check(lib().pkv_timing_enable(1 if on else 0), "pkv_timing_enable")
+
+
+def timing_select(names=None) -> None:
+    """Time only the named kernels (KERNEL_NAMES values); None restores all."""
+    if names is None:
+        mask = 0xFFFFFFFF
+    else:
+        ids = {v: k for k, v in KERNEL_NAMES.items()}
+        mask = 0
+        for nm in names:
+            mask |= 1 << ids[nm]
+    _check(lib().pkv_timing_select(mask), "pkv_timing_select")
 
 
 def timing_collect() -> dict:

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_free_list": (C.c_int, [P, PI32, I32, PI32]),
     "pkv_timing_enable": (C.c_int, [C.c_int]),
     "pkv_timing_collect": (C.c_int, [C.POINTER(pkv_kernel_time), I32, PI32]),
+    "pkv_timing_select": (C.c_int, [C.c_uint32]),
 }
 
 _lib = None

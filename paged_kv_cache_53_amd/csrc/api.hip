@@ -29,6 +29,7 @@ struct TimingRecord {
 struct Timing {
   std::mutex mu;
   bool enabled = false;
+  uint32_t mask = ~0u;   // kernel ids timed while enabled
   std::vector<TimingRecord> pending;
   std::vector<hipEvent_t> spare;
   hipEvent_t open_start = nullptr;  // recorded by timing_before, closed by timing_after
@@ -95,7 +96,7 @@ hipError_t grid_cap(int dtype, int head_dim, int path, int group, int block_size
 void timing_before(int kernel, hipStream_t stream) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.enabled) return;
+  if (!t.enabled || !((t.mask >> kernel) & 1u)) return;
   t.give(t.open_start);
   t.open_start = t.take();
   t.open_kernel = kernel;
@@ -312,6 +313,14 @@ int pkv_timing_enable(int enable) {
   std::lock_guard<std::mutex> g(t.mu);
   t.drop_pending();
   t.enabled = enable != 0;
+  return PKV_OK;
+}
+
+int pkv_timing_select(uint32_t mask) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.drop_pending();
+  t.mask = mask;
   return PKV_OK;
 }
 

@@ -52,6 +52,7 @@ namespace pkv {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -78,22 +79,48 @@ __device__ inline float xor_f(float v, int mask) { return __shfl_xor(v, mask, 64
 
 template <typename T> __device__ inline float to_f32(T x) { return static_cast<float>(x); }
 
-// Stores 4 consecutive output elements.
+// Finished results (outputs and partials) are written through to memory (the sc1 policy).  A
+// store stays in the wave's vector-memory queue until acknowledged, and the loads issued after
+// it cannot retire before it; write-through stores measured 4 % faster on the long workloads
+// than write-back ones.  The cache policy needs inline assembly; the nop after a 16-byte store
+// covers the hazard of a following VALU write to the stored registers, which the compiler
+// cannot see through the asm.  Nothing in the decode kernel reads what these stores write.
+__device__ inline void st_wt(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v));
+}
+__device__ inline void st_wt(void* p, u32x2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" :: "v"(p), "v"(v));
+}
+__device__ inline void st_wt(float* p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1" :: "v"(p), "v"(v));
+}
+__device__ inline void st_wt16(void* p, unsigned bits) {
+  asm volatile("global_store_short %0, %1, off sc1" :: "v"(p), "v"(bits));
+}
+
+// Stores 4 consecutive output elements (16-bit KV types, or fp32 output).
 template <typename T>
 __device__ inline void store4(void* out, int64_t idx, f32x4 v, bool f32out) {
   if (f32out) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+    st_wt(static_cast<float*>(out) + idx, v);
   } else {
+    static_assert(sizeof(T) == 2, "4 elements of a 16-bit type");
     T t[4] = {static_cast<T>(v[0]), static_cast<T>(v[1]), static_cast<T>(v[2]), static_cast<T>(v[3])};
-    uint2 bits;
+    u32x2 bits;
     __builtin_memcpy(&bits, t, 8);
-    *reinterpret_cast<uint2*>(static_cast<T*>(out) + idx) = bits;
+    st_wt(static_cast<T*>(out) + idx, bits);
   }
 }
 template <typename T>
 __device__ inline void store1(void* out, int64_t idx, float v, bool f32out) {
-  if (f32out) static_cast<float*>(out)[idx] = v;
-  else static_cast<T*>(out)[idx] = static_cast<T>(v);
+  if (f32out || sizeof(T) == 4) {
+    st_wt(static_cast<float*>(out) + idx, v);
+  } else {
+    const T t = static_cast<T>(v);
+    unsigned short b;
+    __builtin_memcpy(&b, &t, 2);
+    st_wt16(static_cast<T*>(out) + idx, b);
+  }
 }
 
 // Wave-uniform read of memory no kernel of this launch writes (lengths, block table, unit list):
@@ -183,7 +210,6 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Explicitly waited vector-memory operations.  The tile stream's loads, the early q loads and
 // the work-claim atomic are issued through inline assembly, which the compiler's wait
@@ -241,6 +267,7 @@ struct Tile16 {
 template <typename T>
 struct Unit {
   int s, kvh, part, ntok, nparts;
+  int id_first;       // the partition's first block id, read when the unit is opened
   const int32_t* bt;  // block-table row at the partition's first block
   const T* kbase;     // k_pool + kvh * chunk
   const T* vbase;
@@ -258,6 +285,7 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   u.ntok = min(a.part_tokens, L - tok0);
   u.nparts = (L + a.part_tokens - 1) / a.part_tokens;
   u.bt = a.block_tables + static_cast<int64_t>(u.s) * a.bt_stride + (tok0 >> a.log2_block);
+  u.id_first = ld_uniform(u.bt, 0);
   u.kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(u.kvh) * chunk;
   u.vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(u.kvh) * chunk;
   return u;
@@ -265,18 +293,19 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
 
 // Issues the Tile16::kLoads loads of the 16-token tile at partition offset t0 of a unit (block
 // table row bt, ntok tokens, pools offset to its KV head), completion explicitly waited when E
-// (vload).  Block ids are
-// wave-uniform scalar loads; table entries past the unit's last block are never read (those
-// tokens reuse the first id and are masked in the compute).
+// (vload).  Block ids are wave-uniform scalar loads (the first one was read when the unit was
+// opened); table entries past the unit's last block are never read (those tokens reuse the
+// first id and are masked in the compute).
 template <typename T, int D, int Bsz, bool E>
-__device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int ntok, const T* kbase,
-                                  const T* vbase, int t0, int64_t blk_stride, Tile16<T, D>& R) {
+__device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok,
+                                  const T* kbase, const T* vbase, int t0, int64_t blk_stride,
+                                  Tile16<T, D>& R) {
   constexpr int X = Kv<T>::X;
   using VV = typename Kv<T>::VV;
   constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
   const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int first = t0 / Bsz;
-  int id0 = ld_uniform(bt, first);
+  int id0 = first == 0 ? id_first : ld_uniform(bt, first);
   id0 = min(max(id0, 0), a.num_blocks - 1);
   int id1 = id0;
   if constexpr (NB == 2) {
@@ -432,11 +461,10 @@ struct MfmaMath {
     } else {
       const int64_t pidx = row * a.max_parts + u.part;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        *reinterpret_cast<f32x4*>(a.part_acc + pidx * D + 16 * dt + 4 * g) = acc[dt];
+      for (int dt = 0; dt < D / 16; ++dt) st_wt(a.part_acc + pidx * D + 16 * dt + 4 * g, acc[dt]);
       if (g == 0) {
-        a.part_m[pidx] = m_run;
-        a.part_l[pidx] = l_tot;
+        st_wt(a.part_m + pidx, m_run);
+        st_wt(a.part_l + pidx, l_tot);
       }
     }
   }
@@ -547,10 +575,10 @@ struct VecMath {
       } else {
         const int64_t pidx = row * a.max_parts + u.part;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) a.part_acc[pidx * D + 16 * dt + r16] = o[dt];
+        for (int dt = 0; dt < D / 16; ++dt) st_wt(a.part_acc + pidx * D + 16 * dt + r16, o[dt]);
         if (r16 == 0) {
-          a.part_m[pidx] = m_run[gi];
-          a.part_l[pidx] = lt;
+          st_wt(a.part_m + pidx, m_run[gi]);
+          st_wt(a.part_l + pidx, lt);
         }
       }
     }
@@ -613,6 +641,7 @@ void decode_kernel(DecodeArgs a) {
   if (first >= total) return;
   Unit<T> uc = open_unit<T>(a, first, chunk);   // compute cursor
   Unit<T> ui = uc;                              // issue cursor
+  Unit<T> un_next = uc;                         // the claimed unit after the issue cursor's
   u32x4 qr[Math::QH][NK];
   Math::template load_q<false>(a, uc, qr);
 #pragma unroll
@@ -626,6 +655,7 @@ void decode_kernel(DecodeArgs a) {
   constexpr unsigned kEnded = 2;    // no more units to claim
   constexpr unsigned kQPend = 4;    // qr holds the issue unit's q, not yet parked
   constexpr unsigned kClaimed = 8;  // `pending` holds a claim whose result is not read yet
+  constexpr unsigned kNext = 16;    // un_next holds an opened unit the issue side has not reached
   unsigned fl = 0;
   int ti = 0, tc = 0;
   constexpr int kClaimAhead = 4;   // claim the next unit this many tiles before it is needed
@@ -641,33 +671,44 @@ void decode_kernel(DecodeArgs a) {
   // loads (nothing real left to issue right now) that the compute side must skip.
   // tc_now: the compute cursor's tile offset, passed by value (a reference capture keeps tc in memory)
   auto issue_next = [&](Tile& Y, int tc_now) __attribute__((always_inline)) -> bool {
+    // Opens a claimed unit into un_next (its descriptor and first block id are dependent scalar
+    // reads, done here a few tiles before the switch instead of on its path).
+    auto open_next = [&](int un) __attribute__((always_inline)) {
+      if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
+        un_next = open_unit<T>(a, un, chunk);
+        fl |= kNext;
+      } else {
+        fl |= kEnded;
+      }
+    };
+    if (fl & kClaimed) {
+      // the claim preceded an earlier step's LT tile loads: at most LT outstanding means it returned
+      vm_wait<E, LT>();
+      tie<E>(pending);
+      fl &= ~kClaimed;
+      open_next(__builtin_amdgcn_readfirstlane(pending));
+    }
     if (ti >= ui.ntok && !(fl & (kAhead | kEnded))) {
-      // A claim made by an earlier step preceded that step's LT tile loads: at most LT
-      // outstanding means it has returned.  Without one, claim now and drain.
-      if (!(fl & kClaimed)) {
+      if (!(fl & kNext)) {   // no claim was made ahead: claim now and drain
         claim_unit<E>(a, pending);
         vm_wait<E, 0>();
+        tie<E>(pending);
+        open_next(__builtin_amdgcn_readfirstlane(pending));
       }
-      vm_wait<E, LT>();   // on both paths, so the wait does not hang on a branch condition
-      tie<E>(pending);
-      const int un = __builtin_amdgcn_readfirstlane(pending);
-      fl &= ~kClaimed;
-      if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
-        ui = open_unit<T>(a, un, chunk);
+      if (fl & kNext) {
+        ui = un_next;
         ti = 0;
-        fl |= kAhead;
+        fl = (fl | kAhead) & ~kNext;
         slot_i = slot_c ^ 1;
         if constexpr (Math::kPrefetchQ) {
           Math::template load_q<E>(a, ui, qr);
           fl |= kQPend;
         }
-      } else {
-        fl |= kEnded;
       }
     }
     const bool is_real = ti < ui.ntok;
     // the claim goes before this step's tile loads, so they count towards its wait
-    if (is_real && !(fl & (kClaimed | kEnded)) && ui.ntok - (ti + 16) <= kClaimAhead * 16) {
+    if (is_real && !(fl & (kClaimed | kNext | kEnded)) && ui.ntok - (ti + 16) <= kClaimAhead * 16) {
       claim_unit<E>(a, pending);
       fl |= kClaimed;
     }
@@ -676,7 +717,8 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    issue_tile<T, D, Bsz, E>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.ntok : +uc.ntok,
+    issue_tile<T, D, Bsz, E>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+                             is_real ? +ui.ntok : +uc.ntok,
                              is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
                              is_real ? +ti : tc_now, blk_stride, Y);
     ti += is_real ? 16 : 0;   // a select: a conditional update would put ti in memory

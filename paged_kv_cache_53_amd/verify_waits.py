@@ -25,6 +25,7 @@ import re
 import sys
 from typing import Dict, List, Optional, Set, Tuple
 
+_MAX_CTX = 256   # flag contexts kept apart per block before falling back to one merged state
 _CAP = 64  # vmcnt is 6 bits: an operation with 64 issued after it has retired under any wait
 _STORE = ("global_store", "buffer_store", "scratch_store", "flat_store")
 _VMEM = ("global_", "buffer_", "scratch_", "flat_")
@@ -286,7 +287,7 @@ def check_kernel(body: List[str]) -> List[str]:
             if j is None:
                 continue
             bucket = states.setdefault(j, {})
-            if len(bucket) >= 32 and nctx not in bucket:
+            if len(bucket) >= _MAX_CTX and nctx not in bucket:
                 key = ()   # too many contexts: fall back to the unconstrained one
             else:
                 key = nctx

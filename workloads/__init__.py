@@ -195,11 +195,12 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
             raw = rng_len.lognormal(mean=math.log(3000.0), sigma=1.0, size=256)
             lens = np.clip(np.rint(raw), 16, 32768).astype(np.int32)
         n_blocks = _pool_size([_ceil_div(int(L), bsz) for L in lens], 1.1)
-        # 1024-token partitions: half the partial results of 512 at 20k+ work units, which
-        # measured fastest for this length mix (the partition size is a launch choice)
+        # 2048-token partitions (a launch choice): each partition ends in a store of its
+        # partial result, and fewer, longer partitions measured fastest for this length mix
+        # (512: 1019 us, 1024: 862 us, 2048: 795 us per decode on MI355X)
         return _independent(3, name, seed, 64, 8, 128, bsz, "bf16", lens,
                             _free_order(rng_place, n_blocks, placement), n_blocks,
-                            placement, variant, 1024 if partition_size is None else partition_size)
+                            placement, variant, 2048 if partition_size is None else partition_size)
 
     if config_id == 4:
         # Agent swarm: 20 sequences share one 4000-token prompt (250 blocks), then private
@@ -237,14 +238,15 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
                         variant=variant + ("-copied" if copied_prefix else "-shared"))
 
     if config_id == 5:
-        # Long context: 8 x 65536 tokens, 64 q / 8 kv heads, bf16, B in {8, 16, 32}, P = 512.
+        # Long context: 8 x 65536 tokens, 64 q / 8 kv heads, bf16, B in {8, 16, 32}; 2048-token
+        # partitions (one work unit per wave of the persistent grid; 512 measured 10 % slower).
         bsz = block_size or 16
         n_seqs, L = (2, 2048) if small else (8, 65536)
         lens = np.full(n_seqs, L, dtype=np.int32)
         n_blocks = _pool_size([_ceil_div(L, bsz)] * n_seqs, 1.1)
         return _independent(5, name, seed, 64, 8, 128, bsz, "bf16", lens,
                             _free_order(rng_place, n_blocks, placement), n_blocks,
-                            placement, variant, partition_size or 512)
+                            placement, variant, partition_size or 2048)
 
     raise ValueError(f"unknown config {config_id}")
 
