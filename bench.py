@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    p.add_argument("--copy-blocks", action="store_true",
+                   help="time the copy-on-write block copy kernel alone (4096 random block pairs)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                         "--copy-calibration into the traffic record (CPU only; writes --pmc-out)")
@@ -362,6 +364,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
         return
 
+    if args.copy_blocks:
+        return bench_copy_blocks(args)
+
     w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
                  copied_prefix=args.copied_prefix, partition_size=args.partition_size)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only)
@@ -395,6 +400,50 @@ def main():
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+
+
+def bench_copy_blocks(args):
+    """Copy-on-write block copies on the workload's pool shape: 4096 (src, dst) pairs per call over a
+    pool of 8192 blocks, random placement; bytes = every copied block read once and written once."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_53_amd as pkv
+    import workloads as wl
+    w = wl.build(args.config, block_size=args.block_size)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    n_pairs, N = 4096, 8192
+    kp = torch.empty(pkv.key_pool_shape(N, w.n_kv_heads, w.head_dim, w.block_size, dt), dtype=dt, device="cuda")
+    vp = torch.empty(pkv.value_pool_shape(N, w.n_kv_heads, w.head_dim, w.block_size), dtype=dt, device="cuda")
+    perm = np.random.default_rng([w.seed, 7]).permutation(N)
+    pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], 1).astype(np.int32)).cuda()
+    for _ in range(args.warmup):
+        pkv.copy_blocks(pairs, kp, vp)
+    pkv.timing_select(["copy_blocks"])
+    pkv.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pkv.copy_blocks(pairs, kp, vp)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n, ms = pkv.timing_collect()["copy_blocks"]
+    pkv.timing_enable(False)
+    pkv.timing_select(None)
+    block_bytes = w.n_kv_heads * w.head_dim * w.block_size * w.esize
+    moved = n_pairs * 2 * block_bytes * 2          # both pools, read + write
+    us = ms / n * 1e3
+    achieved = moved / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copies, GB/s moved (read + write)", "value": round(achieved, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} pool shape, {n_pairs} block pairs per call", "block_size": w.block_size,
+                   "block_bytes_per_pool": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
+                     "bytes_per_launch": moved, "avg_launch_us": round(us, 2)}}), flush=True)
 
 
 def sweep(args):

@@ -61,7 +61,8 @@ enum {
   PKV_K_DECODE_PLAN = 2,
   PKV_K_DECODE = 3,
   PKV_K_DECODE_REDUCE = 4,
-  PKV_K_COUNT = 5
+  PKV_K_COPY_BLOCKS = 5,
+  PKV_K_COUNT = 6
 };
 
 /* Text for a status code (static storage, never NULL). */
@@ -96,6 +97,24 @@ int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapp
                           int32_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
                           void* k_pool, void* v_pool, int32_t num_blocks, int32_t n_kv_heads,
                           int32_t head_dim, int32_t block_size, int dtype, void* stream);
+
+/* ---- copy-on-write block copies ----------------------------------------------------
+ * For every pair i, block pairs[2i+1] (dst) of both pools becomes a bit copy of block
+ * pairs[2i] (src), every KV head ("PagedAttention -- Math + Memory Model", section
+ * "Copy-on-write: sharing blocks across samples": a sequence about to write into a block
+ * it shares with another gets a private copy, and its write goes to the copy).  The pairs
+ * are the ones pkv_alloc / pkv_alloc_batch return; apply them before the scatter of the
+ * tokens whose append produced them.  A pair with an id outside [0, num_blocks), or with
+ * src == dst, is skipped (no fault).  Destinations must be distinct and never a source in
+ * the same call (the allocator's pairs always are: a destination is a fresh block), since
+ * the pairs are copied concurrently.
+ *   pairs          device int32 [n_pairs][2], (src, dst)
+ *   k_pool, v_pool device pools of the documented layout, 16-byte aligned, updated in place
+ * One block of one pool is n_kv_heads * head_dim * block_size elements; that byte count
+ * must be a multiple of 16 (PKV_ERR_UNSUPPORTED otherwise). */
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                    int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                    int dtype, void* stream);
 
 /* ---- device half of the on-demand append --------------------------------------
  * One decode step appends one token per batch row.  For every row i with

@@ -77,3 +77,18 @@ def gather_logical(k_pool: np.ndarray, v_pool: np.ndarray, table, L: int):
     K = kb.transpose(0, 3, 1, 2, 4).reshape(nb * B, Hk, D)[:L]
     V = vb.transpose(0, 3, 1, 2).reshape(nb * B, Hk, D)[:L]
     return np.ascontiguousarray(K), np.ascontiguousarray(V)
+
+
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> None:
+    """Copy-on-write: for each (src, dst) pair, block dst of both pools becomes a bit copy of
+    block src, every KV head ("PagedAttention -- Math + Memory Model", section "Copy-on-write:
+    sharing blocks across samples": a sequence about to write into a block it shares gets a
+    private copy of it, and the write lands in the copy).  Pairs are applied in order; ids
+    outside the pool are skipped."""
+    N = k_pool.shape[0]
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if not (0 <= src < N and 0 <= dst < N):
+            continue
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]

@@ -21,7 +21,7 @@ from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PK
 __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
-    "timing_enable", "timing_select", "timing_collect", "lib",
+    "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks",
 ]
 
 
@@ -109,6 +109,18 @@ def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
     _check(lib().pkv_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), T, k.stride(0), v.stride(0),
                                        _ptr(k_pool), _ptr(v_pool), N, Hk, D, B, dtype_code(k_pool),
                                        _stream(stream)), "pkv_reshape_and_cache")
+
+
+def copy_blocks(pairs, k_pool, v_pool, stream=None) -> None:
+    """Copy-on-write: block pairs[i, 1] of both pools becomes a copy of block pairs[i, 0].
+
+    pairs: device int32 [n, 2] (the allocator's (src, dst) pairs)."""
+    import torch
+    N, Hk, D, B = _pool_dims(k_pool, v_pool)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int32 [n, 2] tensor")
+    _check(lib().pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0], N, Hk, D, B,
+                                 dtype_code(k_pool), _stream(stream)), "pkv_copy_blocks")
 
 
 def append_slots(slot_mapping, block_tables, seq_lens, block_size: int, stream=None) -> None:

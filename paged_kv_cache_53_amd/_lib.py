@@ -9,7 +9,8 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-KERNEL_NAMES = {0: "reshape_and_cache", 1: "append_slots", 2: "decode_plan", 3: "decode", 4: "decode_reduce"}
+KERNEL_NAMES = {0: "reshape_and_cache", 1: "append_slots", 2: "decode_plan", 3: "decode", 4: "decode_reduce",
+                5: "copy_blocks"}
 
 
 class pkv_stats(C.Structure):
@@ -33,6 +34,7 @@ SIGNATURES = {
     "pkv_pool_bytes": (SZ, [I32, I32, I32, I32, C.c_int]),
     "pkv_reshape_and_cache": (C.c_int, [P, P, P, I32, I64, I64, P, P, I32, I32, I32, I32, C.c_int, P]),
     "pkv_append_slots": (C.c_int, [P, I32, P, I32, P, I32, P]),
+    "pkv_copy_blocks": (C.c_int, [P, P, P, I32, I32, I32, I32, I32, C.c_int, P]),
     "pkv_paged_attention_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
     "pkv_paged_attention_decode": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                              C.c_float, I32, I32, P, SZ, C.c_int, P]),

@@ -196,6 +196,23 @@ int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapp
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs, int32_t num_blocks,
+                    int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int dtype, void* stream) {
+  if (n_pairs < 0 || !valid_dtype(dtype) || num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0)
+    return PKV_ERR_INVALID;
+  const int64_t block_bytes = static_cast<int64_t>(n_kv_heads) * head_dim * block_size * esize(dtype);
+  if (block_bytes % 16) return PKV_ERR_UNSUPPORTED;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !pairs) return PKV_ERR_INVALID;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(pairs, 4)) return PKV_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_COPY_BLOCKS, st);
+  const hipError_t e = launch_copy_blocks(k_pool, v_pool, pairs, n_pairs, num_blocks, block_bytes, st);
+  timing_after(PKV_K_COPY_BLOCKS, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
                      int32_t block_table_stride, int32_t* seq_lens, int32_t block_size, void* stream) {
   if (num_seqs < 0 || block_table_stride <= 0 || block_size <= 0) return PKV_ERR_INVALID;

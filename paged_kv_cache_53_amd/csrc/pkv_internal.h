@@ -64,6 +64,9 @@ int32_t partition_tokens(int32_t max_seq_len, int32_t partition_size);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream);
+// Copies whole blocks (both pools, every head) for each (src, dst) pair.
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
                                int32_t stride, int32_t* seq_lens, int32_t block_size,
                                hipStream_t stream);

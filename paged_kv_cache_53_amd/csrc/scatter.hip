@@ -9,7 +9,10 @@
 //   value: X scalar stores to (blk, h, c*X + e, off)       -- the value pool keeps
 //          tokens contiguous per head dimension for the decode kernel's PV reads
 // append_slots records, per batch row, the block of the new token's slot in
-// the row's block table and bumps the row's length.
+// the row's block table and bumps the row's length.  copy_blocks makes the
+// private copies of shared blocks that copy-on-write appends ask for.
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -64,7 +67,33 @@ __global__ __launch_bounds__(256) void append_slots_kernel(const int64_t* __rest
   seq_lens[i] = p + 1;
 }
 
+// Copy-on-write: block dst of a pool becomes a copy of block src.  Grid: (pair, pool, slice);
+// each workgroup moves one slice of one block with 16-byte loads and stores.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(void* k_pool, void* v_pool, const int32_t* pairs,
+                                                          int32_t num_blocks, int64_t block_bytes) {
+  const int src = pairs[2 * static_cast<int64_t>(blockIdx.x)];
+  const int dst = pairs[2 * static_cast<int64_t>(blockIdx.x) + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
+  char* pool = static_cast<char*>(blockIdx.y ? v_pool : k_pool);
+  const uint4* s = reinterpret_cast<const uint4*>(pool + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(pool + dst * block_bytes);
+  const int64_t vecs = block_bytes / 16;
+  for (int64_t i = static_cast<int64_t>(blockIdx.z) * blockDim.x + threadIdx.x; i < vecs;
+       i += static_cast<int64_t>(gridDim.z) * blockDim.x)
+    d[i] = s[i];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  if (n_pairs == 0) return hipSuccess;
+  // slices of at least 4 KiB per workgroup, at most 8 per block
+  const int64_t slices = std::min<int64_t>(8, std::max<int64_t>(1, block_bytes / 4096));
+  copy_blocks_kernel<<<dim3(static_cast<unsigned>(n_pairs), 2, static_cast<unsigned>(slices)), dim3(256), 0,
+                       stream>>>(k_pool, v_pool, pairs, num_blocks, block_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream) {
   const int esz = dtype == PKV_F32 ? 4 : 2;

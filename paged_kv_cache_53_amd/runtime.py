@@ -6,7 +6,8 @@ DecodeBatch    a fixed set of sequences decoded together: device block tables an
                a workspace, and ``step()`` -- one decode step of the whole hot path:
                  1. host: the allocator appends one token to every sequence (C++, one call)
                  2. the new slots go to the device through a pinned, double-buffered stage
-                 3. append_slots kernel: new block ids into the device tables, lengths + 1
+                 3. copy_blocks kernel, when an append hit a shared block (copy-on-write)
+                    append_slots kernel: new block ids into the device tables, lengths + 1
                  4. reshape_and_cache kernel: the new tokens' K/V into their slots
                  5. paged decode (plan, main, merge kernels)
                Host work for step i+1 overlaps the GPU work of step i; the host waits only
@@ -20,8 +21,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (Allocator, append_slots, key_pool_shape, paged_attention_decode, reshape_and_cache,
-               value_pool_shape, workspace_size)
+from . import (Allocator, append_slots, copy_blocks, key_pool_shape, paged_attention_decode,
+               reshape_and_cache, value_pool_shape, workspace_size)
 
 
 class PagedKVCache:
@@ -47,11 +48,15 @@ class PagedKVCache:
     def append(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
         """Appends len(k) tokens to seq: slots from the allocator, rows written by the scatter kernel."""
         slots, pairs = self.allocator.alloc(seq, int(k.shape[0]))
-        if pairs:
-            raise NotImplementedError("copy-on-write block copies are not supported by this runtime yet")
+        self.apply_copies(pairs)
         if slots:
             reshape_and_cache(k, v, torch.tensor(slots, dtype=torch.int64, device=self.device),
                               self.k_pool, self.v_pool)
+
+    def apply_copies(self, pairs) -> None:
+        """Makes the private block copies a copy-on-write append asked for (before its scatter)."""
+        if pairs:
+            copy_blocks(torch.tensor(pairs, dtype=torch.int32, device=self.device), self.k_pool, self.v_pool)
 
     def fork(self, parent: int, child: int, n_tokens: int = -1) -> None:
         self.allocator.fork(parent, child, n_tokens)
@@ -96,14 +101,13 @@ class DecodeBatch:
         if self.stage_done[i] is not None:
             self.stage_done[i].synchronize()          # the copy that last read this stage is done
         _, pairs = self.cache.allocator.alloc_batch(self.seq_ids, 1, slots_out=self.slot_stage_np[i])
-        if pairs:
-            raise NotImplementedError("copy-on-write block copies are not supported by this runtime yet")
         self.host_lens += 1
         self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
         self.stage_done[i] = ev
         c = self.cache
+        c.apply_copies(pairs)   # a forked row writing into a shared block gets its private copy first
         append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
         reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool)
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,

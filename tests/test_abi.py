@@ -98,6 +98,13 @@ def test_scatter_and_append_reject_bad_arguments():
     assert g(16, 4, 16, 0, 16, 16, None) == pkv.PKV_ERR_INVALID
     assert g(None, 4, 16, 8, 16, 16, None) == pkv.PKV_ERR_INVALID
     assert g(16, 0, 16, 8, 16, 16, None) == pkv.PKV_OK
+    c = lib.pkv_copy_blocks
+    assert c(16, 16, 16, -1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID            # n_pairs < 0
+    assert c(16, 16, 16, 1, 0, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID              # no pool
+    assert c(16, 16, 16, 1, 10, 1, 4, 1, F16, None) == pkv.PKV_ERR_UNSUPPORTED            # 8-byte blocks
+    assert c(None, 16, 16, 1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID
+    assert c(16, 16, 18, 1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID             # misaligned pairs
+    assert c(None, None, None, 0, 10, 2, 128, 16, F16, None) == pkv.PKV_OK               # nothing to copy
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

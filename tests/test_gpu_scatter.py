@@ -140,3 +140,73 @@ def test_append_slots_matches_allocator_over_steps():
                      w.block_size)
     torch.cuda.synchronize()
     assert torch.equal(before_l, st.seq_lens)
+
+
+# ----------------------------------------------------------------------------- copy-on-write
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f32", 64, 8), ("f16", 128, 32)])
+def test_copy_blocks_bit_exact_vs_oracle(dtype, D, B):
+    log(f"copy_blocks dtype={dtype} D={D} B={B}")
+    rng = np.random.default_rng(11)
+    N, Hk = 40, 3
+    ti, nu, ni = BITS[dtype]
+    dt = TORCH_DTYPE[dtype]
+    kp0 = _random_bits(pkv.key_pool_shape(N, Hk, D, B, dt), dtype, rng)
+    vp0 = _random_bits(pkv.value_pool_shape(N, Hk, D, B), dtype, rng)
+    src = rng.choice(20, size=12, replace=False)
+    dst = 20 + rng.choice(20, size=12, replace=False)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    pairs[3] = [2, 2]            # src == dst: skipped
+    pairs[5] = [-1, 30]          # outside the pool: skipped
+    pairs[7] = [4, N + 2]
+    pairs[9, 0] = pairs[8, 0]    # two copies of one source
+    kp_ref, vp_ref = kp0.copy(), vp0.copy()
+    SC.copy_blocks(kp_ref, vp_ref, pairs.tolist())
+    to_dev = lambda a: torch.from_numpy(a.view(ni)).cuda().view(dt)
+    kp, vp = to_dev(kp0), to_dev(vp0)
+    pkv.copy_blocks(torch.from_numpy(pairs).cuda(), kp, vp)
+    torch.cuda.synchronize()
+    assert np.array_equal(kp.view(ti).cpu().numpy().view(nu), kp_ref)
+    assert np.array_equal(vp.view(ti).cpu().numpy().view(nu), vp_ref)
+
+
+def test_forked_samples_decode_through_copy_on_write():
+    """Parallel sampling from an unaligned prompt, run through the runtime on the GPU: forks share the
+    prompt's blocks, each sample's first decode step copies the shared partial block, and every row's
+    attention output over several steps matches the oracle on that row's own token history."""
+    from paged_kv_cache_53_amd.runtime import DecodeBatch, PagedKVCache
+    from oracle import attention as O
+    log("copy-on-write decode")
+    rng = np.random.default_rng(5)
+    Hq, Hk, D, B, N, dt = 8, 2, 128, 16, 64, torch.bfloat16
+    cache = PagedKVCache(N, B, Hk, D, dt, free_order=rng.permutation(N).tolist(), fill="nan")
+    bits = lambda n: torch.from_numpy(rng.integers(0, 0x3F80, size=(n, Hk, D), dtype=np.int16)).cuda().view(dt)
+    prompt_k, prompt_v = bits(37), bits(37)          # 2 blocks + 5 tokens: the last block is partial
+    cache.append(0, prompt_k, prompt_v)
+    for child in (1, 2, 3):
+        cache.fork(0, child, 37)
+    hist = {s: [prompt_k.clone(), prompt_v.clone()] for s in range(4)}
+    seqs = [0, 1, 2, 3]
+    batch = DecodeBatch(cache, seqs, Hq, 64, partition_size=32)
+    for step in range(3):
+        q = bits(4 * Hq // Hk).view(4, Hq, D)
+        kn, vn = bits(4), bits(4)
+        out = torch.empty_like(q)
+        batch.step(q, kn, vn, out)
+        torch.cuda.synchronize()
+        for r, s in enumerate(seqs):
+            hist[s][0] = torch.cat([hist[s][0], kn[r:r + 1]])
+            hist[s][1] = torch.cat([hist[s][1], vn[r:r + 1]])
+        # expected: attention over each row's own history (logical K/V built from the histories)
+        for r, s in enumerate(seqs):
+            K = wl.storage_to_numpy(hist[s][0].cpu())
+            V = wl.storage_to_numpy(hist[s][1].cpu())
+            L = K.shape[0]
+            # the oracle's pools: the row's history laid out through an identity table
+            kp, vp = SC.empty_pools(-(-L // B), Hk, D, B, np.uint16, 0)
+            SC.reshape_and_cache(K, V, np.arange(L), kp, vp)
+            ref = O.paged_attention_decode(wl.storage_to_numpy(q[r:r + 1].cpu()), kp, vp,
+                                           np.arange(-(-L // B))[None, :], np.array([L]), 1 / np.sqrt(D), "bf16")
+            err = float(np.max(np.abs(out[r].float().cpu().numpy() - ref[0])))
+            assert err <= 2e-2, (step, s, err)
+    st = cache.allocator.stats()
+    assert st["shared_blocks"] == 2    # the two full prompt blocks stay shared; the partial one was copied
