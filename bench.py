@@ -201,7 +201,7 @@ def roofline(res, w=None):
            # measured HBM bytes per launch: the counters' bytes-per-algorithmic-byte ratio of this
            # kernel on this workload, times this run's algorithmic bytes per launch
            "traffic": int(rec["traffic_over_algorithmic"] * per_launch) if rec else None,
-           "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV with G >= 3)",
+           "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV)",
            "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
     if rec:
         out["traffic_detail"] = {"fetch_bytes": int(rec["fetch_over_algorithmic"] * per_launch),

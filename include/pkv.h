@@ -145,7 +145,7 @@ int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* blo
  * Work is split into partitions of partition_size tokens per (row, KV head);
  * each partition keeps its running max, sum and fp32 accumulator, and rows
  * with more than one partition are merged by log-sum-exp rescaling.
- * Accumulation is fp32; for 16-bit KV with G >= 3 the products run on MFMA
+ * Accumulation is fp32; for 16-bit KV the products run on MFMA
  * with the softmax weights rounded to the KV type (the denominator sums the
  * same rounded weights).
  *   out            device [num_seqs][n_q_heads][head_dim] of out_dtype
@@ -177,6 +177,22 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                float scale, int32_t max_seq_len, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, int kv_dtype,
                                void* stream);
+
+/* pkv_paged_attention_decode with flags (pkv_paged_attention_decode is this with flags = 0).
+ *   PKV_DECODE_SHARED_KV  some blocks are read by more than one row of the batch (forked
+ *                         samples, a shared prompt): keep key/value lines cacheable so the
+ *                         rows that reread them hit in L2 / the Infinity Cache.  Without it
+ *                         the tiles are streamed with the non-temporal hint, which is faster
+ *                         when every block is read once.  It changes no result.
+ * Unknown flag bits: PKV_ERR_INVALID. */
+enum { PKV_DECODE_SHARED_KV = 1 };
+int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,
+                                  const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
+                                  void* stream);
 
 /* ---- host block allocator ------------------------------------------------------
  * The block manager of the pages: a free list of physical block ids, a

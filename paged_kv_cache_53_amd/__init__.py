@@ -135,9 +135,15 @@ def workspace_size(num_seqs, n_q_heads, head_dim, max_seq_len, partition_size=51
                                                           partition_size))
 
 
+PKV_DECODE_SHARED_KV = 1
+
+
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
-                           partition_size: int = 512, workspace=None, stream=None) -> None:
-    """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h)."""
+                           partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False) -> None:
+    """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h).
+
+    shared_kv: some blocks are read by more than one row (forks, a shared prompt); keeps them
+    cacheable instead of streaming them.  Results are the same either way."""
     import torch
     N, Hk, D, B = _pool_dims(k_pool, v_pool)
     S, Hq, Dq = q.shape
@@ -148,11 +154,12 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
     need = workspace_size(S, Hq, D, max_seq_len, partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().pkv_paged_attention_decode(
+    _check(lib().pkv_paged_attention_decode_ex(
         _ptr(out), dtype_code(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         block_tables.stride(0), _ptr(seq_lens), S, Hq, Hk, D, B, N, float(scale), int(max_seq_len),
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        dtype_code(k_pool), _stream(stream)), "pkv_paged_attention_decode")
+        dtype_code(k_pool), PKV_DECODE_SHARED_KV if shared_kv else 0, _stream(stream)),
+        "pkv_paged_attention_decode_ex")
 
 
 def timing_enable(on: bool = True) -> None:

@@ -38,6 +38,8 @@ SIGNATURES = {
     "pkv_paged_attention_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
     "pkv_paged_attention_decode": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                              C.c_float, I32, I32, P, SZ, C.c_int, P]),
+    "pkv_paged_attention_decode_ex": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                                C.c_float, I32, I32, P, SZ, C.c_int, C.c_uint32, P]),
     "pkv_allocator_create": (C.c_int, [I32, I32, PI32, C.POINTER(P)]),
     "pkv_allocator_destroy": (None, [P]),
     "pkv_alloc": (C.c_int, [P, I64, I32, PI64, PI32, PI32]),

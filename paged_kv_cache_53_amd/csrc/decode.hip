@@ -28,14 +28,14 @@
 //   vector column).  Values are stored [dim][token] so that a lane's 4
 //   consecutive tokens of one dimension are one 8-byte load -- exactly the
 //   operand the PV product contracts over.
-// * MFMA path (16-bit KV, G >= 3): S^T = K q^T and O^T = V^T P^T with
+// * MFMA path (16-bit KV, any G <= 16): S^T = K q^T and O^T = V^T P^T with
 //   v_mfma_f32_16x16x32_{bf16,f16} and v_mfma_f32_16x16x16{bf16_1k,f16}; the G
 //   query heads of a KV head are the 16-wide N dimension (padded).  The QK
 //   accumulator layout (lane holds tokens 4g..4g+3 for head lane%16) is exactly
 //   the B operand layout of the PV product, so weights never leave their lanes.
 //   The weights are rounded to the KV type for the PV operand, and the
 //   denominator sums the rounded values.
-// * Vector path (fp32 KV, or G <= 2): per-token dot products with a 4-lane
+// * Vector path (fp32 KV): per-token dot products with a 4-lane
 //   cross-group reduction, fp32 weights, FMA accumulation.
 // * q fragments live in LDS (one slot for the unit being computed, one for the
 //   unit being issued), so the tile buffers keep the registers.
@@ -221,20 +221,26 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // vector-memory instructions the pipeline always issues after the operation.  vmcnt counts
 // loads, stores and atomics together and they retire in order, so waiting for at most N
 // outstanding, with N no larger than the number issued since, guarantees completion.
-// The loads carry the non-temporal hint: the key and value stream is read once per call, and
-// keeping it from displacing other lines in L2 and the Infinity Cache measured 5 % faster (the
-// partial results the merge kernel reads next stay resident).
+// Tile loads carry the non-temporal hint by default: the key and value stream is read once per
+// call, and keeping it from displacing other lines in L2 and the Infinity Cache measured 5 %
+// faster (the partial results the merge kernel reads next stay resident).
 // With E false (tiles too large to keep three in registers without spilling, where a spill of
 // an in-flight register would be wrong) every helper is the ordinary compiler-tracked form.
-template <bool E>
+// NT selects the non-temporal hint (the caller's choice: off when blocks are shared by rows of
+// the batch and are worth keeping in cache).
+template <bool E, bool NT>
 __device__ inline void vload(u32x4& d, const void* p) {
-  if constexpr (E) asm volatile("global_load_dwordx4 %0, %1, off nt" : "+v"(d) : "v"(p));
-  else d = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  if constexpr (E && NT) asm volatile("global_load_dwordx4 %0, %1, off nt" : "+v"(d) : "v"(p));
+  else if constexpr (E) asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(d) : "v"(p));
+  else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  else d = *static_cast<const u32x4*>(p);
 }
-template <bool E>
+template <bool E, bool NT>
 __device__ inline void vload(u32x2& d, const void* p) {
-  if constexpr (E) asm volatile("global_load_dwordx2 %0, %1, off nt" : "+v"(d) : "v"(p));
-  else d = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  if constexpr (E && NT) asm volatile("global_load_dwordx2 %0, %1, off nt" : "+v"(d) : "v"(p));
+  else if constexpr (E) asm volatile("global_load_dwordx2 %0, %1, off" : "+v"(d) : "v"(p));
+  else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  else d = *static_cast<const u32x2*>(p);
 }
 // waits until at most N vector-memory operations are outstanding
 template <bool E, int N> __device__ inline void vm_wait() {
@@ -296,7 +302,7 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
 // (vload).  Block ids are wave-uniform scalar loads (the first one was read when the unit was
 // opened); table entries past the unit's last block are never read (those tokens reuse the
 // first id and are masked in the compute).
-template <typename T, int D, int Bsz, bool E>
+template <typename T, int D, int Bsz, bool E, bool NT>
 __device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok,
                                   const T* kbase, const T* vbase, int t0, int64_t blk_stride,
                                   Tile16<T, D>& R) {
@@ -317,11 +323,11 @@ __device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int id
   const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
   const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
 #pragma unroll
-  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) vload<E>(R.kf[ks], kb + ks * 4 * Bsz * X);
+  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) vload<E, NT>(R.kf[ks], kb + ks * 4 * Bsz * X);
   const int bv = (NB == 2 && g >= 2) ? id1 : id0;
   const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) vload<E>(R.vf[dt], vb + dt * 16 * Bsz);
+  for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(R.vf[dt], vb + dt * 16 * Bsz);
 }
 
 // q fragments of one query head hq of row s: lane (r16, g) holds the 16-byte vectors
@@ -333,7 +339,7 @@ __device__ inline void load_q_head(const DecodeArgs& a, int s, int hq, u32x4* qr
   const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(s) * a.n_q_heads + hq) * D;
 #pragma unroll
   for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) {
-    vload<kAsync>(qr[ks], qrow + Kv<T>::X * (4 * ks + g));
+    vload<kAsync, false>(qr[ks], qrow + Kv<T>::X * (4 * ks + g));   // q rows are reread per partition
   }
 }
 
@@ -372,7 +378,7 @@ __device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, _Float16) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
 }
 
-// G >= 3 query heads of one KV head on 16-bit KV: S^T = K q^T (16 tokens x 16 heads, G of
+// G <= 16 query heads of one KV head on 16-bit KV: S^T = K q^T (16 tokens x 16 heads, G of
 // them real) and O^T += V^T P^T on MFMA.  The QK accumulator's lane layout (tokens 4g..4g+3
 // for head lane%16) is the PV B operand, so the weights never leave their lanes; they are
 // rounded to the KV type for the operand and the denominator sums the rounded values.
@@ -471,7 +477,7 @@ struct MfmaMath {
 };
 
 // ------------------------------------------------------------------------------ vector math
-// G <= 2 query heads on 16-bit KV, G <= 4 on fp32 KV (GM >= G): fp32 dot products per token (a lane's
+// G <= 4 query heads on fp32 KV (GM >= G): fp32 dot products per token (a lane's
 // 4ks+g vectors, then a 4-lane cross-group reduction), softmax over the tile's 16 tokens with
 // in-row reductions, fp32 weights, and FMA accumulation of the value columns (lane: dim
 // 16dt + lane%16 over tokens 4g..4g+3, summed over the 4 groups when the unit ends).
@@ -620,7 +626,7 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
 // issue it re-issues the current tile's loads (a filler the compute side skips), so each step
 // issues the same loads on every path.  The next unit is claimed a few tiles before it is
 // needed.
-template <typename T, int D, int Bsz, class Math>
+template <typename T, int D, int Bsz, class Math, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
   using Tile = Tile16<T, D>;
@@ -717,7 +723,7 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    issue_tile<T, D, Bsz, E>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+    issue_tile<T, D, Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
                              is_real ? +ui.ntok : +uc.ntok,
                              is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
                              is_real ? +ti : tc_now, blk_stride, Y);
@@ -851,33 +857,37 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename T, int D, class Math>
+template <typename T, int D, class Math, bool NT>
 const void* kernel_ptr_b(int block_size) {
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<T, D, 8, Math>);
-    case 16: return reinterpret_cast<const void*>(&decode_kernel<T, D, 16, Math>);
-    case 32: return reinterpret_cast<const void*>(&decode_kernel<T, D, 32, Math>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<T, D, 8, Math, NT>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<T, D, 16, Math, NT>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<T, D, 32, Math, NT>);
     default: return nullptr;
   }
 }
 
 template <typename T, int D>
-const void* kernel_ptr_d(int path, int group, int block_size) {
+const void* kernel_ptr_d(int path, int group, int block_size, bool nt) {
   if (path == 1) {
-    if constexpr (sizeof(T) == 2) return kernel_ptr_b<T, D, MfmaMath<T, D>>(block_size);
+    if constexpr (sizeof(T) == 2)
+      return nt ? kernel_ptr_b<T, D, MfmaMath<T, D>, true>(block_size)
+                : kernel_ptr_b<T, D, MfmaMath<T, D>, false>(block_size);
     return nullptr;
   }
-  if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>>(block_size);
-  if (group == 2) return kernel_ptr_b<T, D, VecMath<T, D, 2>>(block_size);
-  // 16-bit KV with three or more heads per group takes the MFMA path
-  if constexpr (sizeof(T) == 4) return kernel_ptr_b<T, D, VecMath<T, D, 4>>(block_size);
+  // the vector path serves fp32 KV only (always streamed): 16-bit KV takes the MFMA path
+  if constexpr (sizeof(T) == 4) {
+    if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>, true>(block_size);
+    if (group == 2) return kernel_ptr_b<T, D, VecMath<T, D, 2>, true>(block_size);
+    return kernel_ptr_b<T, D, VecMath<T, D, 4>, true>(block_size);
+  }
   return nullptr;
 }
 
 template <typename T>
-const void* main_kernel_ptr(int head_dim, int path, int group, int block_size) {
-  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size)
-                         : kernel_ptr_d<T, 64>(path, group, block_size);
+const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt) {
+  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt)
+                         : kernel_ptr_d<T, 64>(path, group, block_size, nt);
 }
 
 }  // namespace
@@ -889,11 +899,11 @@ hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, int32_t grid,
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, bool nt, int32_t grid,
                               hipStream_t st) {
-  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size)
-                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size)
-                                      : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size);
+  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt)
+                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt)
+                                      : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(64), args, 0, st);
@@ -915,9 +925,10 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 }
 
 hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap) {
-  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size)
-                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size)
-                                      : main_kernel_ptr<__bf16>(head_dim, path, group, block_size);
+  // both cache policies compile to the same code shape: the streamed variant stands for both
+  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true)
+                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true)
+                                      : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true);
   if (!fn) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -72,7 +72,8 @@ hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, in
                                hipStream_t stream);
 hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // path: 0 = vector, 1 = MFMA
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path,
+// nt: stream the key/value tiles with the non-temporal hint (otherwise ordinary cached loads)
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, bool nt,
                               int32_t grid, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.

@@ -58,6 +58,10 @@ class PagedKVCache:
         if pairs:
             copy_blocks(torch.tensor(pairs, dtype=torch.int32, device=self.device), self.k_pool, self.v_pool)
 
+    def has_shared_blocks(self) -> bool:
+        """Whether some block is referenced by more than one sequence (decode then keeps blocks cacheable)."""
+        return self.allocator.stats()["shared_blocks"] > 0
+
     def fork(self, parent: int, child: int, n_tokens: int = -1) -> None:
         self.allocator.fork(parent, child, n_tokens)
 
@@ -111,11 +115,13 @@ class DecodeBatch:
         append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
         reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool)
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
-                               self.max_seq_len, self.partition_size, workspace=self.workspace)
+                               self.max_seq_len, self.partition_size, workspace=self.workspace,
+                               shared_kv=c.has_shared_blocks())
         self.steps += 1
 
     def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
         """Attention over the current tokens without appending (no host work, no scatter)."""
         c = self.cache
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
-                               self.max_seq_len, self.partition_size, workspace=self.workspace)
+                               self.max_seq_len, self.partition_size, workspace=self.workspace,
+                               shared_kv=c.has_shared_blocks())

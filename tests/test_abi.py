@@ -98,6 +98,9 @@ def test_scatter_and_append_reject_bad_arguments():
     assert g(16, 4, 16, 0, 16, 16, None) == pkv.PKV_ERR_INVALID
     assert g(None, 4, 16, 8, 16, 16, None) == pkv.PKV_ERR_INVALID
     assert g(16, 0, 16, 8, 16, 16, None) == pkv.PKV_OK
+    d = lib.pkv_paged_attention_decode_ex
+    assert d(16, F16, 16, 16, 16, 16, 8, 16, 1, 8, 2, 128, 16, 100, 0.1, 128, 512, 256, 1 << 30, F16,
+             2, None) == pkv.PKV_ERR_INVALID                                              # unknown flag
     c = lib.pkv_copy_blocks
     assert c(16, 16, 16, -1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID            # n_pairs < 0
     assert c(16, 16, 16, 1, 0, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID              # no pool

@@ -61,6 +61,8 @@ def test_shared_prefix_equals_copied_prefix_bitwise():
     assert a.alloc.stats()["shared_blocks"] == 400 // 16
     oa, ob = a.decode(), b.decode()
     assert torch.equal(_bits(oa), _bits(ob))
+    # the cache-policy flag (kept-cacheable loads for shared blocks) changes no bit of the result
+    assert torch.equal(_bits(a.decode(shared_kv=True)), _bits(oa))
     ref = oracle_rows(copied, range(copied.num_seqs))
     assert max_abs_err(oa, ref, rows=range(copied.num_seqs)) <= TOL["f16"]
 
