@@ -12,6 +12,8 @@ Parts (each file's docstring cites the passages it follows):
 * ``scatter``      -- writing token rows into physical slots, and reading a
                       sequence's logical K/V back through its block table (O3)
 * ``attention``    -- decode attention over the gathered K/V, in fp64 (O4)
+* ``fp8``          -- the FP8 E4M3 codes of a quantised cache, with per-tensor
+                      scales (the quantised-KV extension)
 
 Source pages (cited by title and section):
 
@@ -27,4 +29,4 @@ Every function here is pinned by tests under ``tests/`` against values the
 pages print, closed forms, brute force or library routines; none is marked
 "parity unpinned".
 """
-from . import memory_math, allocator, scatter, attention  # noqa: F401
+from . import memory_math, allocator, scatter, attention, fp8  # noqa: F401

@@ -3,10 +3,10 @@
 Test infrastructure only (see the package docstring).
 
 The pages say what the paged kernel does and leave the arithmetic to the
-standard definition: it "reads the block table and gathers keys and values
-from the scattered physical blocks for the QK^T and the value-weighted sum"
-("PagedAttention -- Math + Memory Model", section "PagedAttention: blocks and
-the block table"; "KV-cache paging in vLLM", section "The Attention Kernel
+standard definition: it follows the block table and collects keys and values
+from their scattered physical blocks for the score product and the weighted
+sum of values ("PagedAttention -- Math + Memory Model", section
+"PagedAttention: blocks and the block table"; "KV-cache paging in vLLM", section "The Attention Kernel
 Change": the kernel takes the block table as an extra input and gathers
 blocks during the attention computation).  So the oracle is that plain
 definition, written out:
@@ -27,12 +27,15 @@ definition, written out:
 Readings: the decode token attends to itself (seq_lens count it and the
 scatter runs first); scale is a parameter (1/sqrt(head_dim) in every
 workload); no partitioning -- the split-context merge is exact in real
-arithmetic, so the oracle never splits.
+arithmetic, so the oracle never splits.  A quantised cache (FP8 E4M3 codes with
+per-tensor scales, ``fp8``) is read as the values it represents, and the same
+definition applies to them (``paged_attention_decode_fp8``).
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
 from .scatter import gather_logical
 
 
@@ -81,4 +84,20 @@ def paged_attention_decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray
         L = int(seq_lens[s])
         K, V = gather_logical(k_pool, v_pool, block_tables[s], L)
         out[s] = attention_logical(to_f64(q[s], dtype), to_f64(K, dtype), to_f64(V, dtype), scale)
+    return out
+
+
+def paged_attention_decode_fp8(q: np.ndarray, q_dtype: str, k_pool: np.ndarray, v_pool: np.ndarray,
+                               k_scale: float, v_scale: float, block_tables: np.ndarray,
+                               seq_lens: np.ndarray, scale: float, rows=None) -> np.ndarray:
+    """Decode attention over a quantised cache: the same attention as ``paged_attention_decode``,
+    on the values the cache holds, k_scale * value(code) and v_scale * value(code)
+    (``fp8.dequantize``).  q: [S, Hq, D] storage of q_dtype; pools: uint8 E4M3 codes."""
+    S, Hq, D = q.shape
+    out = np.full((S, Hq, D), np.nan, dtype=np.float64)
+    for s in (range(S) if rows is None else rows):
+        L = int(seq_lens[s])
+        K, V = gather_logical(k_pool, v_pool, block_tables[s], L)
+        out[s] = attention_logical(to_f64(q[s], q_dtype), fp8.dequantize(K, k_scale),
+                                   fp8.dequantize(V, v_scale), scale)
     return out

@@ -2,22 +2,26 @@
 
 Test infrastructure only (see the package docstring).
 
-The pages name quantising the cached keys and values as the next memory lever after paging
-("Reserve-for-max KV cache fits four of eight agents on RDNA4", section "The order of the memory
-levers"; "KV-Cache Optimization & PagedAttention for Long-Context Agents", introduction) but fix no
-format.  The reading taken here is the OCP 8-bit floating point format E4M3, which MI355X
-computes on natively:
+The pages name quantising the cached keys and values as the memory lever that follows paging: an
+8-bit KV cache halves the bytes each sequence's attention reads ("Contiguous vs Paged KV Cache on
+RDNA4", section "The order of the memory levers"; "KV-Cache Optimization & PagedAttention for
+Long-Context Agents", introduction), but they fix no format.  The reading taken here is the OCP
+8-bit floating point format E4M3, which MI355X converts natively:
 
 * one sign bit, four exponent bits with bias 7, three mantissa bits;
 * exponent field e > 0: value = (-1)^s * 2^(e - 7) * (1 + m/8);
 * e = 0: value = (-1)^s * 2^-6 * (m/8) (subnormals and the two zeros);
 * no infinities; the code S.1111.111 is NaN, so the largest finite magnitude is 2^8 * 1.75 = 448.
 
-Encoding a real x (a per-tensor scale s is divided out first, x/s) takes the nearest
-representable value, ties to the code with an even mantissa (round to nearest even), and
-saturates any magnitude above 448 to +-448; NaN encodes to NaN.  The decoder is the definition
-above; the encoder is a brute-force nearest search over all 254 finite codes, which is slow and
-obviously right.
+Encoding a real x takes the nearest representable value, ties to the code with an even
+mantissa (round to nearest even), and saturates any magnitude above 448 to +-448; NaN encodes to
+NaN.  The decoder is the definition above; the encoder is a brute-force nearest search over all
+254 finite codes, which is slow and obviously right.
+
+A cache stores an element x with a per-tensor scale s as the code of x / s and reads it back as
+s * value(code) (``quantize`` / ``dequantize``).  The quotient is rounded to fp32 before the
+code is chosen: that rounding can move a value onto a midpoint between two codes, so it is part
+of what decides the code, and it is the rounding a device that quantises in fp32 performs.
 """
 from __future__ import annotations
 
@@ -96,3 +100,16 @@ def encode_fast(x: np.ndarray, scale: float = 1.0) -> np.ndarray:
     code = code | np.where(np.signbit(v), 0x80, 0)
     code = np.where(np.isnan(v), 0x7F, code)
     return code.astype(np.uint8)
+
+
+def quantize(x: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of x / scale for a cache with per-tensor scale ``scale``: the quotient of the fp32
+    values is rounded to fp32 (IEEE division), then encoded (nearest, ties even, saturating)."""
+    xf = np.asarray(x, dtype=np.float32)
+    qf = (xf / np.float32(scale)).astype(np.float32)
+    return encode_fast(qf.astype(np.float64))
+
+
+def dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
+    """The values a cache with per-tensor scale ``scale`` holds: scale * value(code), in fp64."""
+    return float(scale) * decode(codes)

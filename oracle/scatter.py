@@ -16,12 +16,16 @@ x elements):
           element (blk, h, d, off)    = value of token (blk, off), head h, dim d
 
 Slot s names token position s % B of physical block s // B.  Everything
-here moves raw bits (uint16 / uint32 / float32 arrays are copied, never
-converted), so -0.0 and NaN payloads survive.
+here moves raw bits (uint8 / uint16 / uint32 / float32 arrays are copied, never
+converted), so -0.0 and NaN payloads survive.  A quantised cache stores one-byte
+FP8 E4M3 codes (x = 16) that ``reshape_and_cache_fp8`` computes from the new
+rows before the same bit copy.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import fp8
 
 
 def chunk_elems(esize: int) -> int:
@@ -35,7 +39,7 @@ def empty_pools(num_blocks: int, n_kv_heads: int, head_dim: int, block_size: int
     x = chunk_elems(esize)
     k = np.empty((num_blocks, n_kv_heads, head_dim // x, block_size, x), dtype=storage_dtype)
     v = np.empty((num_blocks, n_kv_heads, head_dim, block_size), dtype=storage_dtype)
-    ui = {2: np.uint16, 4: np.uint32}[esize]
+    ui = {1: np.uint8, 2: np.uint16, 4: np.uint32}[esize]
     k.view(ui)[...] = fill_bits
     v.view(ui)[...] = fill_bits
     return k, v
@@ -60,6 +64,15 @@ def reshape_and_cache(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
         blk, off = divmod(s, B)
         k_pool[blk, :, :, off, :] = k[t].reshape(Hk, C, x)
         v_pool[blk, :, :, off] = v[t]
+
+
+def reshape_and_cache_fp8(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                          k_pool: np.ndarray, v_pool: np.ndarray, k_scale: float, v_scale: float) -> None:
+    """The scatter into a quantised cache: every element of the new rows is stored as its E4M3
+    code under the pool's per-tensor scale (``fp8.quantize``), then placed like any other row.
+    k, v: [T, Hk, D] float32 (the exact values of the source rows); pools: uint8 codes."""
+    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+    reshape_and_cache(fp8.quantize(k, k_scale), fp8.quantize(v, v_scale), slot_mapping, k_pool, v_pool)
 
 
 def gather_logical(k_pool: np.ndarray, v_pool: np.ndarray, table, L: int):
