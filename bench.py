@@ -18,7 +18,10 @@ decode kernel's roofline (HIP events on the kernel's stream), and the fp64
 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16]
-                    [--placement random|identity] [--no-cpu-baseline] [--sweep]
+                    [--placement random|identity] [--kv-dtype native|fp8] [--no-cpu-baseline] [--sweep]
+
+--kv-dtype fp8 runs the same workload on a quantised cache (FP8 E4M3 codes, per-tensor scales;
+q and outputs keep the workload's type): bytes then count one byte per cached element.
 """
 from __future__ import annotations
 
@@ -50,6 +53,8 @@ def parse():
     p.add_argument("--placement", default="random", choices=["random", "identity"])
     p.add_argument("--partition-size", type=int, default=None, help="default: the workload's own")
     p.add_argument("--copied-prefix", action="store_true", help="config 4: private prefix copies")
+    p.add_argument("--kv-dtype", default="native", choices=["native", "fp8"],
+                   help="fp8: the cache stores FP8 E4M3 codes (per-tensor scales)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--sweep", action="store_true", help="config-5 block-size x placement sweep (decode only)")
@@ -61,7 +66,7 @@ def parse():
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                         "--copy-calibration into the traffic record (CPU only; writes --pmc-out)")
-    p.add_argument("--pmc-out", default=os.path.join(ROOT, "profiles", "decode_traffic_llama70b_gqa.json"))
+    p.add_argument("--pmc-out", default=None, help="default: the workload's traffic record under profiles/")
     p.add_argument("--pmc-command", default="", help="the command lines that produced the CSVs (recorded)")
     return p.parse_args()
 
@@ -74,8 +79,13 @@ def build_batch(w, fill="randn", extra_tokens=0):
     import workloads as wl
     from paged_kv_cache_53_amd.runtime import DecodeBatch, PagedKVCache
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-    cache = PagedKVCache(w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, dt, device="cuda",
-                         free_order=w.free_order.tolist(), fill=fill)
+    if w.kv_format == "fp8":
+        cache = PagedKVCache(w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, torch.float8_e4m3fn,
+                             device="cuda", free_order=w.free_order.tolist(), fill=fill, k_scale=w.k_scale,
+                             v_scale=w.v_scale)
+    else:
+        cache = PagedKVCache(w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, dt, device="cuda",
+                             free_order=w.free_order.tolist(), fill=fill)
     for op in w.prompt_ops:
         if op["op"] == "alloc":
             k, v = wl.kv_rows(w, op["seq"], op["pos"], op["n"], device="cuda")
@@ -94,7 +104,7 @@ def kv_bytes(w, lens):
     """Algorithmic bytes one decode reads: K+V of every valid token, plus the block-table entries."""
     import numpy as np
     lens = np.asarray(lens, dtype=np.int64)
-    kv = int(lens.sum()) * 2 * w.n_kv_heads * w.head_dim * w.esize
+    kv = int(lens.sum()) * 2 * w.n_kv_heads * w.head_dim * w.kv_esize
     table = int(((lens + w.block_size - 1) // w.block_size).sum()) * 4
     return kv, table
 
@@ -175,10 +185,15 @@ def workload_key(w):
             "partition_size": w.partition_size, "placement": w.placement}
 
 
+def traffic_record_path(w):
+    suffix = "_fp8" if w.kv_format == "fp8" else ""
+    return os.path.join(ROOT, "profiles", f"decode_traffic_{w.name}{suffix}.json")
+
+
 def measured_traffic(w):
     """HBM bytes per decode launch from the committed counter record, or None when the record
     was taken on other kernel sources or another workload."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic_llama70b_gqa.json")
+    path = traffic_record_path(w)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -201,12 +216,14 @@ def roofline(res, w=None):
            # measured HBM bytes per launch: the counters' bytes-per-algorithmic-byte ratio of this
            # kernel on this workload, times this run's algorithmic bytes per launch
            "traffic": int(rec["traffic_over_algorithmic"] * per_launch) if rec else None,
-           "kernel": "decode_kernel (persistent paged decode, MFMA policy for 16-bit KV)",
+           "kernel": "decode_kernel (persistent paged decode on MFMA, "
+                     + ("FP8 E4M3 KV widened in registers" if w is not None and w.kv_format == "fp8" else "16-bit KV")
+                     + ")",
            "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
     if rec:
         out["traffic_detail"] = {"fetch_bytes": int(rec["fetch_over_algorithmic"] * per_launch),
                                  "write_bytes": int(rec["write_over_algorithmic"] * per_launch),
-                                 "source": "profiles/decode_traffic_llama70b_gqa.json"}
+                                 "source": os.path.relpath(traffic_record_path(w), ROOT)}
     return out
 
 
@@ -247,8 +264,7 @@ def pmc_summary(args):
     import numpy as np
 
     import workloads as wl
-    w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
-                 copied_prefix=args.copied_prefix, partition_size=args.partition_size)
+    w = make_workload(args)
     # decode dispatch j of the profiled bench run attends over the prompt (L - 1 tokens) plus the
     # j + 1 tokens appended so far; a --decode-only run appends nothing
     prompt = w.seq_lens.astype(np.int64) - 1
@@ -273,8 +289,9 @@ def pmc_summary(args):
                         "write_bytes": int(w_vals[-1] * w_scale * 1024)},
         "command": args.pmc_command,
     }
-    os.makedirs(os.path.dirname(args.pmc_out), exist_ok=True)
-    with open(args.pmc_out, "w") as f:
+    out_path = args.pmc_out or traffic_record_path(w)
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec), flush=True)
@@ -304,7 +321,8 @@ def _oracle_sample(w, budget_s, cores, used):
     from oracle import attention as O
     from oracle import scatter as SC
     from oracle.allocator import BlockAllocatorModel
-    st = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    fp8 = w.kv_format == "fp8"
+    st = np.uint8 if fp8 else {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
     order = np.random.default_rng([w.seed, 99]).permutation(w.num_seqs)
     done, kvb, tb, spent = [], 0, 0, 0.0
     for r in order.tolist():
@@ -318,11 +336,19 @@ def _oracle_sample(w, budget_s, cores, used):
         kp, vp = SC.empty_pools(a.num_blocks, w.n_kv_heads, w.head_dim, w.block_size, st, 0)
         slots, _ = a.alloc(seq, L)
         K, V = wl.logical_kv(w, r)
-        SC.reshape_and_cache(wl.storage_to_numpy(K), wl.storage_to_numpy(V), np.array(slots), kp, vp)
+        if fp8:
+            kf = O.to_f64(wl.storage_to_numpy(K), w.dtype).astype(np.float32)
+            vf = O.to_f64(wl.storage_to_numpy(V), w.dtype).astype(np.float32)
+            SC.reshape_and_cache_fp8(kf, vf, np.array(slots), kp, vp, w.k_scale, w.v_scale)
+        else:
+            SC.reshape_and_cache(wl.storage_to_numpy(K), wl.storage_to_numpy(V), np.array(slots), kp, vp)
         q = wl.storage_to_numpy(wl.q_values(w))[r:r + 1]
         table = np.array([a.block_table(seq)])
         t0 = time.perf_counter()
-        O.paged_attention_decode(q, kp, vp, table, np.array([L]), w.scale, w.dtype)
+        if fp8:
+            O.paged_attention_decode_fp8(q, w.dtype, kp, vp, w.k_scale, w.v_scale, table, np.array([L]), w.scale)
+        else:
+            O.paged_attention_decode(q, kp, vp, table, np.array([L]), w.scale, w.dtype)
         spent += time.perf_counter() - t0
         done.append(r)
         x, y = kv_bytes(w, [L])
@@ -332,10 +358,18 @@ def _oracle_sample(w, budget_s, cores, used):
             "kind": "oracle", "seqs_per_s": round(len(done) / spent, 3),
             "sample": f"{len(done)} of {w.num_seqs} rows of {w.name} (seeded order), "
                       f"{int(sum(int(w.seq_lens[r]) for r in done))} tokens, {spent:.1f} s of fp64 numpy "
-                      f"(gather through the block table + attention), host cores available {cores}"}
+                      f"(gather through the block table{' + dequantisation' if fp8 else ''} + attention), "
+                      f"host cores available {cores}"}
 
 
 # ------------------------------------------------------------------------------------- main
+def make_workload(args):
+    import workloads as wl
+    w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
+                 copied_prefix=args.copied_prefix, partition_size=args.partition_size)
+    return wl.quantised(w) if args.kv_dtype == "fp8" else w
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -367,8 +401,7 @@ def main():
     if args.copy_blocks:
         return bench_copy_blocks(args)
 
-    w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
-                 copied_prefix=args.copied_prefix, partition_size=args.partition_size)
+    w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only)
     total_s = res["total_s"]
     gbps = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
@@ -382,6 +415,7 @@ def main():
         "config": {"workload": w.name, "seqs": w.num_seqs, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size, "partition_size": w.partition_size,
                    "placement": w.placement, "total_tokens_at_start": int(res["lens0"].sum()),
+                   "kv_dtype": "fp8_e4m3 (per-tensor scales)" if w.kv_format == "fp8" else w.dtype,
                    "seed": w.seed, "step": "decode_only" if args.decode_only else
                    "host append + stage + append_slots + scatter + decode"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -393,7 +427,7 @@ def main():
         # unique bytes: the shared prompt is stored (and mostly fetched from HBM) once
         prefix = 4000
         uniq_tokens = prefix + int(sum(int(L) - prefix for L in res["lens0"]))
-        line["unique_kv_bytes_per_step"] = uniq_tokens * 2 * w.n_kv_heads * w.head_dim * w.esize
+        line["unique_kv_bytes_per_step"] = uniq_tokens * 2 * w.n_kv_heads * w.head_dim * w.kv_esize
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)

@@ -22,6 +22,8 @@
  *   A failed launch returns PKV_ERR_HIP.
  * - Element types: PKV_F32 (float), PKV_F16 (IEEE binary16), PKV_BF16
  *   (bfloat16).  Copies move raw bits (NaN payloads and -0.0 survive).
+ *   A quantised cache holds PKV_FP8_E4M3 codes in its pools (see the FP8
+ *   section below); rows, q and results are never FP8.
  * - Integer sizes are int32_t, token slots are int64_t.
  *
  * Storage layout of the pools (row-major, X = 16 bytes / element size, so X
@@ -52,7 +54,7 @@ enum {
   PKV_ERR_HIP = -5          /* the HIP runtime reported an error */
 };
 
-enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 };
 
 /* Kernel ids reported by pkv_timing_collect. */
 enum {
@@ -71,7 +73,8 @@ const char* pkv_status_string(int status);
 /* Library ABI version, bumped on any incompatible change. */
 int pkv_version(void);
 
-/* Bytes of ONE pool (key or value) for the given shape; 0 if the shape is invalid. */
+/* Bytes of ONE pool (key or value) for the given shape and pool element type (PKV_FP8_E4M3
+ * included); 0 if the shape is invalid. */
 size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
                       int32_t block_size, int dtype);
 
@@ -92,7 +95,8 @@ size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
  *   slot_mapping  device, int64 [num_tokens]
  *   k_pool/v_pool device, pools of the documented layout
  * Two tokens with the same slot in one call: undefined which one lands.
- * Bits are copied unchanged.  head_dim must be a multiple of X. */
+ * Bits are copied unchanged.  head_dim must be a multiple of X.  dtype: PKV_F32,
+ * PKV_F16 or PKV_BF16 (FP8 pools take pkv_reshape_and_cache_fp8). */
 int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
                           int32_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
                           void* k_pool, void* v_pool, int32_t num_blocks, int32_t n_kv_heads,
@@ -110,8 +114,9 @@ int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapp
  * the pairs are copied concurrently.
  *   pairs          device int32 [n_pairs][2], (src, dst)
  *   k_pool, v_pool device pools of the documented layout, 16-byte aligned, updated in place
- * One block of one pool is n_kv_heads * head_dim * block_size elements; that byte count
- * must be a multiple of 16 (PKV_ERR_UNSUPPORTED otherwise). */
+ * One block of one pool is n_kv_heads * head_dim * block_size elements of dtype (any pool
+ * type, PKV_FP8_E4M3 included); that byte count must be a multiple of 16
+ * (PKV_ERR_UNSUPPORTED otherwise). */
 int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
                     int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                     int dtype, void* stream);
@@ -165,7 +170,9 @@ int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* blo
  *                  bytes, 256-byte aligned; its contents on entry do not matter; two
  *                  calls in flight at once must not share it
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; G = 1..16 for
- * 16-bit KV (1..3 on the vector path, 4..16 on MFMA), G = 1..4 for fp32 KV. */
+ * 16-bit KV (MFMA, heads padded to 16), G = 1..4 for fp32 KV.  kv_dtype is the
+ * type of q and of the pools (PKV_F32, PKV_F16 or PKV_BF16; FP8 pools take
+ * pkv_paged_attention_decode_fp8). */
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t head_dim,
                                           int32_t max_seq_len, int32_t partition_size);
 
@@ -193,6 +200,48 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
                                   int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
                                   void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
                                   void* stream);
+
+/* ---- quantised cache: FP8 E4M3 pools ------------------------------------------------
+ * Quantising the cached keys and values is the memory lever the pages put after paging: an
+ * 8-bit cache halves the bytes each sequence's attention reads ("Contiguous vs Paged KV Cache
+ * on RDNA4", section "The order of the memory levers"; "KV-Cache Optimization & PagedAttention
+ * for Long-Context Agents", introduction).  The format is OCP FP8 E4M3: sign, 4 exponent bits
+ * (bias 7), 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite 448.  Each pool
+ * has one per-tensor scale: an element x is stored as code(x / scale) and represents
+ * scale * value(code).  The pools keep the documented layout with one-byte elements, so
+ * X = 16 codes per key vector and head_dim must be a multiple of 16. */
+
+/* The scatter of pkv_reshape_and_cache into FP8 pools: for every token t with an in-range
+ * slot, each element x of k[t] / v[t] (src_dtype: PKV_F32, PKV_F16 or PKV_BF16) is stored as
+ * the E4M3 code of x / k_scale (x / v_scale for values): the quotient is the fp32 IEEE
+ * division of the fp32 value of x, then the nearest code, ties to the even mantissa;
+ * magnitudes of 448 and above become +-448 and NaN becomes 0x7F.  Strides, alignment and
+ * skipped slots as for pkv_reshape_and_cache (strides in src_dtype elements).  Scales must be
+ * positive and finite (PKV_ERR_INVALID otherwise). */
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                              int32_t num_tokens, int64_t k_token_stride, int64_t v_token_stride,
+                              void* k_pool, void* v_pool, int32_t num_blocks, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t block_size, int src_dtype, float k_scale,
+                              float v_scale, void* stream);
+
+/* Decode attention over FP8 pools: pkv_paged_attention_decode_ex on the values the pools
+ * represent, K = k_scale * value(code), V = v_scale * value(code).
+ *   q        device [num_seqs][n_q_heads][head_dim] of q_dtype (PKV_BF16 or PKV_F16; PKV_F32:
+ *            PKV_ERR_UNSUPPORTED), 16-byte aligned rows
+ *   out      of out_dtype = q_dtype or PKV_F32
+ * The codes are widened exactly to q_dtype in registers and the products run on MFMA with fp32
+ * accumulation; k_scale is folded into the score scale (scale * k_scale, rounded to fp32) and
+ * v_scale multiplies the accumulated values.  The softmax weights are rounded to q_dtype for the
+ * value product, as for 16-bit pools.  Scales must be positive and finite.  Supported shapes,
+ * flags, workspace and every other argument as for pkv_paged_attention_decode_ex (G = 1..16). */
+int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int q_dtype,
+                                   const void* k_pool, const void* v_pool, float k_scale, float v_scale,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, float scale, int32_t max_seq_len,
+                                   int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, void* stream);
 
 /* ---- host block allocator ------------------------------------------------------
  * The block manager of the pages: a free list of physical block ids, a

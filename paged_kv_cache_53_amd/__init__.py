@@ -8,6 +8,10 @@ nothing falls back if the library is missing.
     k_pool, v_pool = torch.empty(key_pool_shape(...)), torch.empty(value_pool_shape(...))
     reshape_and_cache(k, v, slot_mapping, k_pool, v_pool)
     paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale, max_seq_len)
+
+A quantised cache has pools of torch.float8_e4m3fn (or uint8) holding FP8 E4M3 codes, one
+per-tensor scale per pool: pass k_scale / v_scale to reshape_and_cache and
+paged_attention_decode.
 """
 from __future__ import annotations
 
@@ -16,7 +20,7 @@ from typing import List, Optional, Sequence, Tuple
 
 from . import _lib
 from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PKV_ERR_OOM,  # noqa: F401
-                   PKV_ERR_UNSUPPORTED, PKV_F16, PKV_F32, PKV_OK, KERNEL_NAMES, LibraryNotBuilt)
+                   PKV_ERR_UNSUPPORTED, PKV_F16, PKV_F32, PKV_FP8_E4M3, PKV_OK, KERNEL_NAMES, LibraryNotBuilt)
 
 __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
@@ -49,9 +53,16 @@ def _check(status: int, what: str) -> None:
 
 
 def dtype_code(t) -> int:
+    """Element type code of a tensor or dtype: float32, float16, bfloat16, and for pools of a
+    quantised cache float8_e4m3fn or uint8 (E4M3 codes)."""
     import torch
     dt = t if isinstance(t, torch.dtype) else t.dtype
-    return {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}[dt]
+    return {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+            torch.float8_e4m3fn: PKV_FP8_E4M3, torch.uint8: PKV_FP8_E4M3}[dt]
+
+
+def _is_fp8_pool(t) -> bool:
+    return dtype_code(t) == PKV_FP8_E4M3
 
 
 def _x(dtype) -> int:
@@ -97,8 +108,11 @@ def _pool_dims(k_pool, v_pool):
     return N, Hk, D, B
 
 
-def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
-    """Writes k[t], v[t] ([T, Hk, D], token rows may be strided) into slot slot_mapping[t]."""
+def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None, k_scale=None, v_scale=None) -> None:
+    """Writes k[t], v[t] ([T, Hk, D], token rows may be strided) into slot slot_mapping[t].
+
+    FP8 pools (float8_e4m3fn / uint8) store the E4M3 codes of k / k_scale and v / v_scale
+    (both scales required); other pools take rows of their own dtype, copied bit for bit."""
     N, Hk, D, B = _pool_dims(k_pool, v_pool)
     T = k.shape[0]
     if k.shape != (T, Hk, D) or v.shape != (T, Hk, D) or slot_mapping.shape != (T,):
@@ -106,6 +120,18 @@ def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
     for t in (k, v):
         if t.stride(2) != 1 or t.stride(1) != D:
             raise ValueError("k/v rows must be contiguous within a token")
+    if _is_fp8_pool(k_pool):
+        if k_scale is None or v_scale is None:
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        if k.dtype != v.dtype:
+            raise ValueError("k and v must have one dtype")
+        _check(lib().pkv_reshape_and_cache_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), T, k.stride(0), v.stride(0),
+                                               _ptr(k_pool), _ptr(v_pool), N, Hk, D, B, dtype_code(k),
+                                               float(k_scale), float(v_scale), _stream(stream)),
+               "pkv_reshape_and_cache_fp8")
+        return
+    if k_scale is not None or v_scale is not None:
+        raise ValueError("scales apply to FP8 pools only")
     _check(lib().pkv_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), T, k.stride(0), v.stride(0),
                                        _ptr(k_pool), _ptr(v_pool), N, Hk, D, B, dtype_code(k_pool),
                                        _stream(stream)), "pkv_reshape_and_cache")
@@ -139,11 +165,14 @@ PKV_DECODE_SHARED_KV = 1
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
-                           partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False) -> None:
+                           partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False,
+                           k_scale=None, v_scale=None) -> None:
     """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h).
 
     shared_kv: some blocks are read by more than one row (forks, a shared prompt); keeps them
-    cacheable instead of streaming them.  Results are the same either way."""
+    cacheable instead of streaming them.  Results are the same either way.
+    FP8 pools (float8_e4m3fn / uint8): attention over k_scale * value(code) and
+    v_scale * value(code), with q in bf16 or f16."""
     import torch
     N, Hk, D, B = _pool_dims(k_pool, v_pool)
     S, Hq, Dq = q.shape
@@ -154,11 +183,24 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
     need = workspace_size(S, Hq, D, max_seq_len, partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    flags = PKV_DECODE_SHARED_KV if shared_kv else 0
+    if _is_fp8_pool(k_pool):
+        if k_scale is None or v_scale is None:
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        _check(lib().pkv_paged_attention_decode_fp8(
+            _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), float(k_scale),
+            float(v_scale), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), S, Hq, Hk, D, B, N,
+            float(scale), int(max_seq_len), int(partition_size), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), flags, _stream(stream)),
+            "pkv_paged_attention_decode_fp8")
+        return
+    if k_scale is not None or v_scale is not None:
+        raise ValueError("scales apply to FP8 pools only")
     _check(lib().pkv_paged_attention_decode_ex(
         _ptr(out), dtype_code(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         block_tables.stride(0), _ptr(seq_lens), S, Hq, Hk, D, B, N, float(scale), int(max_seq_len),
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        dtype_code(k_pool), PKV_DECODE_SHARED_KV if shared_kv else 0, _stream(stream)),
+        dtype_code(k_pool), flags, _stream(stream)),
         "pkv_paged_attention_decode_ex")
 
 

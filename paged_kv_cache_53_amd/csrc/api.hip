@@ -11,8 +11,12 @@ namespace pkv {
 namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-inline int esize(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+inline int esize(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_FP8_E4M3 ? 1 : 2; }
+// element types of rows, q and results
 inline bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+// element types a pool may hold
+inline bool valid_pool_dtype(int d) { return valid_dtype(d) || d == PKV_FP8_E4M3; }
+inline bool valid_scale(float s) { return s > 0.f && s <= 3.402823466e38f; }   // positive, finite
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int log2i(int v) {
   int l = 0;
@@ -68,13 +72,14 @@ Timing& timing() {
 std::mutex cap_mu;
 std::unordered_map<int64_t, int32_t> cap_cache;
 
-hipError_t grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap) {
+hipError_t grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size, int32_t* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4)
-  const int variant = path == 1 ? 3 : (group == 1 ? 0 : group == 2 ? 1 : 2);
-  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 4 + variant) * 64) +
+  // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4),
+  // the MFMA path one per storage type
+  const int variant = path == 1 ? (kv_fp8 ? 4 : 3) : (group == 1 ? 0 : group == 2 ? 1 : 2);
+  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 8 + variant) * 64) +
                       block_size;
   {
     std::lock_guard<std::mutex> g(cap_mu);
@@ -84,7 +89,7 @@ hipError_t grid_cap(int dtype, int head_dim, int path, int group, int block_size
       return hipSuccess;
     }
   }
-  e = decode_main_grid_cap(dtype, head_dim, path, group, block_size, cap);
+  e = decode_main_grid_cap(dtype, kv_fp8, head_dim, path, group, block_size, cap);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> g(cap_mu);
   cap_cache[key] = *cap;
@@ -161,7 +166,7 @@ int pkv_version(void) { return 1; }
 
 size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                       int dtype) {
-  if (num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || !valid_dtype(dtype))
+  if (num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || !valid_pool_dtype(dtype))
     return 0;
   const int X = 16 / esize(dtype);
   if (head_dim % X) return 0;
@@ -196,9 +201,36 @@ int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapp
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                              int64_t k_token_stride, int64_t v_token_stride, void* k_pool, void* v_pool,
+                              int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                              int src_dtype, float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || !valid_dtype(src_dtype) || num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || !valid_scale(k_scale) || !valid_scale(v_scale))
+    return PKV_ERR_INVALID;
+  const int es = esize(src_dtype);
+  if (head_dim % 16) return PKV_ERR_INVALID;   // 16 codes per key vector
+  const int64_t row = static_cast<int64_t>(n_kv_heads) * head_dim;
+  const int64_t ks = k_token_stride == 0 ? row : k_token_stride;
+  const int64_t vs = v_token_stride == 0 ? row : v_token_stride;
+  if (ks < row || vs < row || (ks * es) % 16 || (vs * es) % 16) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_INVALID;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID;
+  ScatterArgs a{k, v, slot_mapping, k_pool, v_pool, ks, vs, num_tokens, num_blocks, n_kv_heads,
+                head_dim, block_size};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_RESHAPE_AND_CACHE, st);
+  const hipError_t e = launch_reshape_and_cache_fp8(a, src_dtype, k_scale, v_scale, st);
+  timing_after(PKV_K_RESHAPE_AND_CACHE, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs, int32_t num_blocks,
                     int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int dtype, void* stream) {
-  if (n_pairs < 0 || !valid_dtype(dtype) || num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+  if (n_pairs < 0 || !valid_pool_dtype(dtype) || num_blocks <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0)
     return PKV_ERR_INVALID;
   const int64_t block_bytes = static_cast<int64_t>(n_kv_heads) * head_dim * block_size * esize(dtype);
@@ -249,16 +281,23 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                        workspace_bytes, kv_dtype, 0u, stream);
 }
 
-int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const void* k_pool,
-                                  const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,
-                                  const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
-                                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
-                                  int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
-                                  void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points.  q_dtype: the type of q (and of out unless out is fp32); kv_fp8: the
+// pools hold E4M3 codes with scales k_scale / v_scale (else they hold q_dtype).
+int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                bool kv_fp8, float k_scale, float v_scale, const int32_t* block_tables,
+                int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                uint32_t flags, void* stream) {
+  const int kv_dtype = q_dtype;   // the compute type of the kernels
   if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV)) return PKV_ERR_INVALID;
   // ---- shape and type checks
   if (!valid_dtype(kv_dtype) || !(out_dtype == kv_dtype || out_dtype == PKV_F32)) return PKV_ERR_INVALID;
+  if (kv_fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale))) return PKV_ERR_INVALID;
   if (num_seqs < 0 || n_q_heads <= 0 || n_q_heads > 65535 || n_kv_heads <= 0 || (n_q_heads % n_kv_heads) ||
       num_blocks <= 0 ||
       max_seq_len < 0 || partition_size < 0 || (partition_size % 32) || block_size <= 0 ||
@@ -269,7 +308,7 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
   const int group = n_q_heads / n_kv_heads;
   int path;
   if (kv_dtype == PKV_F32) {
-    if (group > 4) return PKV_ERR_UNSUPPORTED;
+    if (kv_fp8 || group > 4) return PKV_ERR_UNSUPPORTED;   // a quantised cache takes bf16 or f16 q
     path = 0;
   } else {
     if (group > 16) return PKV_ERR_UNSUPPORTED;
@@ -315,10 +354,11 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
   a.part_tokens = P;
   a.max_parts = max_parts;
   a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = (kv_fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  a.v_scale = kv_fp8 ? v_scale : 1.f;
 
   int32_t cap = 0;
-  if (grid_cap(kv_dtype, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
+  if (grid_cap(kv_dtype, kv_fp8, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
   const int32_t grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -327,7 +367,7 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
   timing_after(PKV_K_DECODE_PLAN, st);
   if (e != hipSuccess) return PKV_ERR_HIP;
   timing_before(PKV_K_DECODE, st);
-  e = launch_decode_main(a, kv_dtype, head_dim, path, (flags & PKV_DECODE_SHARED_KV) == 0, grid, st);
+  e = launch_decode_main(a, kv_dtype, kv_fp8, head_dim, path, (flags & PKV_DECODE_SHARED_KV) == 0, grid, st);
   timing_after(PKV_K_DECODE, st);
   if (e != hipSuccess) return PKV_ERR_HIP;
   if (max_parts > 1) {
@@ -337,6 +377,33 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,
+                                  const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
+                                  void* stream) {
+  return decode_impl(out, out_dtype, q, kv_dtype, k_pool, v_pool, false, 1.f, 1.f, block_tables,
+                     block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size,
+                     num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags, stream);
+}
+
+int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool,
+                                   const void* v_pool, float k_scale, float v_scale, const int32_t* block_tables,
+                                   int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  return decode_impl(out, out_dtype, q, q_dtype, k_pool, v_pool, true, k_scale, v_scale, block_tables,
+                     block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size,
+                     num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags, stream);
 }
 
 int pkv_timing_enable(int enable) {

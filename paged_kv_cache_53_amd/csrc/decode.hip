@@ -35,6 +35,12 @@
 //   the B operand layout of the PV product, so weights never leave their lanes.
 //   The weights are rounded to the KV type for the PV operand, and the
 //   denominator sums the rounded values.
+// * Quantised KV (FP8 E4M3 codes with per-tensor scales, q and output in bf16
+//   or f16): the same MFMA products after widening the codes in registers to
+//   q's type, which holds every E4M3 value exactly.  A key vector is 16 codes
+//   (16 bytes), so a lane's q fragments take the matching dims; the key scale
+//   is folded into the score scale and the value scale into the output.  The
+//   tile's bytes halve, its loads stay the same in number.
 // * Vector path (fp32 KV): per-token dot products with a 4-lane
 //   cross-group reduction, fp32 weights, FMA accumulation.
 // * q fragments live in LDS (one slot for the unit being computed, one for the
@@ -242,6 +248,13 @@ __device__ inline void vload(u32x2& d, const void* p) {
   else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
   else d = *static_cast<const u32x2*>(p);
 }
+template <bool E, bool NT>
+__device__ inline void vload(unsigned& d, const void* p) {
+  if constexpr (E && NT) asm volatile("global_load_dword %0, %1, off nt" : "+v"(d) : "v"(p));
+  else if constexpr (E) asm volatile("global_load_dword %0, %1, off" : "+v"(d) : "v"(p));
+  else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const unsigned*>(p));
+  else d = *static_cast<const unsigned*>(p);
+}
 // waits until at most N vector-memory operations are outstanding
 template <bool E, int N> __device__ inline void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
@@ -250,12 +263,18 @@ template <bool E, int N> __device__ inline void vm_wait() {
 // orders every later use of r after the preceding wait
 template <bool E, typename R> __device__ inline void tie(R& r) { if constexpr (E) asm volatile("" : "+v"(r)); }
 
+// Storage element of a quantised cache: one FP8 E4M3 code.
+struct E4M3 {
+  unsigned char bits;
+};
+
 // Storage traits: X elements per 16-byte key vector; VV holds 4 consecutive tokens of one
 // value dimension.
 template <typename T> struct Kv;
 template <> struct Kv<__bf16> { static constexpr int X = 8; using VV = u32x2; };
 template <> struct Kv<_Float16> { static constexpr int X = 8; using VV = u32x2; };
 template <> struct Kv<float> { static constexpr int X = 4; using VV = u32x4; };
+template <> struct Kv<E4M3> { static constexpr int X = 16; using VV = unsigned; };
 
 // Register-resident tile of 16 tokens.  Keys: lane (token lane%16, group g = lane/16) holds
 // the 16-byte vectors 4ks+g of its token's row (the A operand of the MFMA QK product, and the
@@ -330,16 +349,21 @@ __device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int id
   for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(R.vf[dt], vb + dt * 16 * Bsz);
 }
 
-// q fragments of one query head hq of row s: lane (r16, g) holds the 16-byte vectors
-// 4ks+g of the head's row, matching the key fragments.
+// q fragments of one query head hq of row s (q of type T, keys stored as KV): lane (r16, g)
+// holds, in D / XQ / 4 16-byte vectors of XQ elements, the dims of the key vectors 4k+g its
+// tile fragment holds (q vector j: the (j % R)-th XQ-element piece of key vector 4(j / R) + g,
+// R = key elements per key vector / XQ, so 2 for 16-code FP8 key vectors and 16-bit q).
 // kAsync: issued with vload (the caller waits explicitly); otherwise ordinary loads.
-template <typename T, int D, bool kAsync>
+template <typename T, typename KV, int D, bool kAsync>
 __device__ inline void load_q_head(const DecodeArgs& a, int s, int hq, u32x4* qr) {
+  constexpr int XQ = 16 / sizeof(T);
+  constexpr int R = Kv<KV>::X / XQ;
   const int g = threadIdx.x >> 4;
   const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(s) * a.n_q_heads + hq) * D;
 #pragma unroll
-  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) {
-    vload<kAsync, false>(qr[ks], qrow + Kv<T>::X * (4 * ks + g));   // q rows are reread per partition
+  for (int j = 0; j < D / XQ / 4; ++j) {
+    const int dim0 = Kv<KV>::X * (4 * (j / R) + g) + XQ * (j % R);
+    vload<kAsync, false>(qr[j], qrow + dim0);   // q rows are reread per partition
   }
 }
 
@@ -378,15 +402,49 @@ __device__ inline f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c, _Float16) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, c, 0, 0, 0);
 }
 
+// 4 E4M3 codes (a little-endian word) as 4 elements of T, exactly: every E4M3 value is
+// representable in bf16 and in f16.  The packed gfx950 conversion with unit scale.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ inline u32x2 widen4(unsigned w, __bf16) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);   // codes 0, 1
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);    // codes 2, 3
+  unsigned l, h;
+  __builtin_memcpy(&l, &lo, 4);
+  __builtin_memcpy(&h, &hi, 4);
+  return u32x2{l, h};
+}
+__device__ inline u32x2 widen4(unsigned w, _Float16) {
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  unsigned l, h;
+  __builtin_memcpy(&l, &lo, 4);
+  __builtin_memcpy(&h, &hi, 4);
+  return u32x2{l, h};
+}
+// 8 codes (two words) as the 8-element MFMA operand of type T
+template <typename T>
+__device__ inline typename Vec8<T>::type widen8(unsigned w0, unsigned w1) {
+  const u32x2 a = widen4(w0, T{}), b = widen4(w1, T{});
+  const u32x4 v = {a[0], a[1], b[0], b[1]};
+  typename Vec8<T>::type r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
 // G <= 16 query heads of one KV head on 16-bit KV: S^T = K q^T (16 tokens x 16 heads, G of
 // them real) and O^T += V^T P^T on MFMA.  The QK accumulator's lane layout (tokens 4g..4g+3
 // for head lane%16) is the PV B operand, so the weights never leave their lanes; they are
 // rounded to the KV type for the operand and the denominator sums the rounded values.
-template <typename T, int D>
+// KV = T: 16-bit keys and values; KV = E4M3: codes widened to T in registers, the key scale
+// folded into scale_log2 by the caller and the value scale applied to the results.
+template <typename T, int D, typename KV = T>
 struct MfmaMath {
   static constexpr int QH = 1;            // q fragment sets parked per unit
+  static constexpr int NQ = D / 32;       // q vectors per lane: one per 32-wide MFMA k-step
   static constexpr bool kPrefetchQ = true;
-  using Tile = Tile16<T, D>;
+  static constexpr bool kQuant = !std::is_same<KV, T>::value;
+  using Tile = Tile16<KV, D>;
   f32x4 acc[D / 16];
   float m_run, l_run;
 
@@ -398,20 +456,25 @@ struct MfmaMath {
   }
   // lanes of padded heads (h >= G) read head 0 of the group: their columns are discarded
   template <bool kAsync>
-  __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
+  __device__ static void load_q(const DecodeArgs& a, const Unit<KV>& u, u32x4 (*qr)[NQ]) {
     const int r16 = threadIdx.x & 15;
-    load_q_head<T, D, kAsync>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
+    load_q_head<T, KV, D, kAsync>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
   }
-  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
+  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     using V8 = typename Vec8<T>::type;
     const int g = threadIdx.x >> 4;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < Tile::NK; ++ks) {
-      const u32x4 qb = q_lds[0][ks][threadIdx.x];
+    for (int j = 0; j < NQ; ++j) {
+      const u32x4 qb = q_lds[0][j][threadIdx.x];
       V8 qv, kv;
       __builtin_memcpy(&qv, &qb, 16);
-      __builtin_memcpy(&kv, &R.kf[ks], 16);
+      if constexpr (kQuant) {   // key vector j / 2 holds 16 codes: q vector j takes half j % 2
+        const u32x4 kw = R.kf[j / 2];
+        kv = (j % 2) ? widen8<T>(kw[2], kw[3]) : widen8<T>(kw[0], kw[1]);
+      } else {
+        __builtin_memcpy(&kv, &R.kf[j], 16);
+      }
       sc = mfma_16x16x32(kv, qv, sc);
     }
     float x[4];
@@ -441,7 +504,9 @@ struct MfmaMath {
     __builtin_memcpy(&pb, pt, 8);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 va = R.vf[dt];
+      u32x2 va;
+      if constexpr (kQuant) va = widen4(R.vf[dt], T{});
+      else va = R.vf[dt];
       if (partial) {
         T vt[4];
         __builtin_memcpy(vt, &va, 8);
@@ -453,21 +518,23 @@ struct MfmaMath {
       acc[dt] = mfma_16x16x16(va, pb, acc[dt] * alpha, T{});
     }
   }
-  // the normalised output when the row has one partition, else (max, sum, accumulator)
-  __device__ void finish(const DecodeArgs& a, const Unit<T>& u) {
+  // the normalised output when the row has one partition, else (max, sum, accumulator); with
+  // quantised values the accumulator is scaled by the value scale
+  __device__ void finish(const DecodeArgs& a, const Unit<KV>& u) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     float l_tot = l_run + xor_f(l_run, 16);
     l_tot += xor_f(l_tot, 32);
     if (r16 >= a.group) return;
     const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + r16;
     if (u.nparts == 1) {
-      const float inv = 1.f / l_tot;
+      const float inv = kQuant ? a.v_scale / l_tot : 1.f / l_tot;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) store4<T>(a.out, row * D + 16 * dt + 4 * g, acc[dt] * inv, a.out_f32);
     } else {
       const int64_t pidx = row * a.max_parts + u.part;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) st_wt(a.part_acc + pidx * D + 16 * dt + 4 * g, acc[dt]);
+      for (int dt = 0; dt < D / 16; ++dt)
+        st_wt(a.part_acc + pidx * D + 16 * dt + 4 * g, kQuant ? acc[dt] * a.v_scale : acc[dt]);
       if (g == 0) {
         st_wt(a.part_m + pidx, m_run);
         st_wt(a.part_l + pidx, l_tot);
@@ -486,6 +553,7 @@ struct VecMath {
   static constexpr int QH = GM;
   static constexpr bool kPrefetchQ = GM == 1;   // more heads: q is loaded at the unit switch
   using Tile = Tile16<T, D>;
+  static constexpr int NQ = Tile::NK;
   static constexpr int X = Kv<T>::X;
   float acc[GM][D / 16];
   float m_run[GM], l_run[GM];
@@ -501,12 +569,12 @@ struct VecMath {
     }
   }
   template <bool kAsync>
-  __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[Tile::NK]) {
+  __device__ static void load_q(const DecodeArgs& a, const Unit<T>& u, u32x4 (*qr)[NQ]) {
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi)
-      load_q_head<T, D, kAsync>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
+      load_q_head<T, T, D, kAsync>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
   }
-  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[Tile::NK][64], int t0, int ntok, float scale_log2) {
+  __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     const bool partial = t0 + 16 > ntok;
     float kv[Tile::NK][X];
@@ -626,18 +694,19 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
 // issue it re-issues the current tile's loads (a filler the compute side skips), so each step
 // issues the same loads on every path.  The next unit is claimed a few tiles before it is
 // needed.
-template <typename T, int D, int Bsz, class Math, bool NT>
+// KV: the storage type of the pools (the tile's element); Math carries the compute type.
+template <typename KV, int D, int Bsz, class Math, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
-  using Tile = Tile16<T, D>;
-  constexpr int NK = Tile::NK;
+  using Tile = Tile16<KV, D>;
+  constexpr int NQ = Math::NQ;
   // explicitly waited loads while three tiles fit in 96 registers (32 per tile)
   constexpr bool E = sizeof(Tile) <= 32 * 4;
   constexpr int LT = Tile::kLoads;   // every step issues exactly this many tile loads
   const int64_t chunk = static_cast<int64_t>(D) * Bsz;
   const int64_t blk_stride = chunk * a.n_kv_heads;
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
-  __shared__ u32x4 q_lds[2][Math::QH][NK][64];   // q fragments: compute unit's and issue unit's
+  __shared__ u32x4 q_lds[2][Math::QH][NQ][64];   // q fragments: compute unit's and issue unit's
 
   int pending = 0;
   claim_unit<E>(a, pending);
@@ -645,15 +714,15 @@ void decode_kernel(DecodeArgs a) {
   tie<E>(pending);
   const int first = __builtin_amdgcn_readfirstlane(pending);
   if (first >= total) return;
-  Unit<T> uc = open_unit<T>(a, first, chunk);   // compute cursor
-  Unit<T> ui = uc;                              // issue cursor
-  Unit<T> un_next = uc;                         // the claimed unit after the issue cursor's
-  u32x4 qr[Math::QH][NK];
+  Unit<KV> uc = open_unit<KV>(a, first, chunk);   // compute cursor
+  Unit<KV> ui = uc;                              // issue cursor
+  Unit<KV> un_next = uc;                         // the claimed unit after the issue cursor's
+  u32x4 qr[Math::QH][NQ];
   Math::template load_q<false>(a, uc, qr);
 #pragma unroll
   for (int h = 0; h < Math::QH; ++h)
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) q_lds[0][h][ks][threadIdx.x] = qr[h][ks];
+    for (int j = 0; j < NQ; ++j) q_lds[0][h][j][threadIdx.x] = qr[h][j];
   int slot_c = 0, slot_i = 0;
   // Wave-uniform state bits, packed in one word: separate flags captured by the lambdas below
   // get their stores merged through a pointer select, which puts them in scratch.
@@ -670,7 +739,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < Math::QH; ++h)
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) q_lds[slot][h][ks][threadIdx.x] = qr[h][ks];
+      for (int j = 0; j < NQ; ++j) q_lds[slot][h][j][threadIdx.x] = qr[h][j];
   };
 
   // Fills Y with the next tile of the issue stream; returns false when Y only holds filler
@@ -681,7 +750,7 @@ void decode_kernel(DecodeArgs a) {
     // reads, done here a few tiles before the switch instead of on its path).
     auto open_next = [&](int un) __attribute__((always_inline)) {
       if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
-        un_next = open_unit<T>(a, un, chunk);
+        un_next = open_unit<KV>(a, un, chunk);
         fl |= kNext;
       } else {
         fl |= kEnded;
@@ -723,7 +792,7 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    issue_tile<T, D, Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+    issue_tile<KV, D, Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
                              is_real ? +ui.ntok : +uc.ntok,
                              is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
                              is_real ? +ti : tc_now, blk_stride, Y);
@@ -751,7 +820,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < Math::QH; ++h)
 #pragma unroll
-          for (int ks = 0; ks < NK; ++ks) tie<E>(qr[h][ks]);
+          for (int j = 0; j < NQ; ++j) tie<E>(qr[h][j]);
         park_q(slot_i);
         fl &= ~kQPend;
       }
@@ -761,7 +830,7 @@ void decode_kernel(DecodeArgs a) {
     // X was issued two steps ago; each of the two steps since issued LT tile loads
     vm_wait<E, 2 * LT>();
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) tie<E>(X.kf[ks]);
+    for (int ks = 0; ks < Tile::NK; ++ks) tie<E>(X.kf[ks]);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) tie<E>(X.vf[dt]);
     if (!x_real) return true;   // a filler: nothing to compute this step
@@ -857,24 +926,30 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename T, int D, class Math, bool NT>
+template <typename KV, int D, class Math, bool NT>
 const void* kernel_ptr_b(int block_size) {
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<T, D, 8, Math, NT>);
-    case 16: return reinterpret_cast<const void*>(&decode_kernel<T, D, 16, Math, NT>);
-    case 32: return reinterpret_cast<const void*>(&decode_kernel<T, D, 32, Math, NT>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT>);
     default: return nullptr;
   }
 }
 
+// T: the type of q and of the outputs; fp8: the pools hold E4M3 codes (MFMA path only)
 template <typename T, int D>
-const void* kernel_ptr_d(int path, int group, int block_size, bool nt) {
+const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8) {
   if (path == 1) {
-    if constexpr (sizeof(T) == 2)
+    if constexpr (sizeof(T) == 2) {
+      if (fp8)
+        return nt ? kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, true>(block_size)
+                  : kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, false>(block_size);
       return nt ? kernel_ptr_b<T, D, MfmaMath<T, D>, true>(block_size)
                 : kernel_ptr_b<T, D, MfmaMath<T, D>, false>(block_size);
+    }
     return nullptr;
   }
+  if (fp8) return nullptr;
   // the vector path serves fp32 KV only (always streamed): 16-bit KV takes the MFMA path
   if constexpr (sizeof(T) == 4) {
     if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>, true>(block_size);
@@ -885,9 +960,9 @@ const void* kernel_ptr_d(int path, int group, int block_size, bool nt) {
 }
 
 template <typename T>
-const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt) {
-  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt)
-                         : kernel_ptr_d<T, 64>(path, group, block_size, nt);
+const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt, bool fp8) {
+  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt, fp8)
+                         : kernel_ptr_d<T, 64>(path, group, block_size, nt, fp8);
 }
 
 }  // namespace
@@ -899,11 +974,12 @@ hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, bool nt, int32_t grid,
-                              hipStream_t st) {
-  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt)
-                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt)
-                                      : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt);
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, bool nt,
+                              int32_t grid, hipStream_t st) {
+  const void* fn =
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt, kv_fp8)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt, kv_fp8)
+                         : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt, kv_fp8);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(64), args, 0, st);
@@ -924,11 +1000,12 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
   return hipGetLastError();
 }
 
-hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap) {
+hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size,
+                                int32_t* cap) {
   // both cache policies compile to the same code shape: the streamed variant stands for both
-  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true)
-                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true)
-                                      : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true);
+  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true, kv_fp8)
+                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true, kv_fp8)
+                                      : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true, kv_fp8);
   if (!fn) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

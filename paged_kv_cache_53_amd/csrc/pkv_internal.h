@@ -51,7 +51,9 @@ struct DecodeArgs {
   int32_t part_tokens;   // partition size in tokens (multiple of 32)
   int32_t max_parts;
   int32_t out_f32;       // 1: out is float, 0: out has the KV type
-  float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
+  float scale_log2;      // scale * log2(e) (times the key scale of a quantised cache): scores
+                         // are kept in the base-2 domain
+  float v_scale;         // value scale of a quantised cache (1 otherwise)
 };
 
 // Workspace carve-up shared by the size query and the launcher.
@@ -64,6 +66,9 @@ int32_t partition_tokens(int32_t max_seq_len, int32_t partition_size);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream);
+// The scatter into an FP8 E4M3 cache: sources of src_dtype, codes of x / scale.
+hipError_t launch_reshape_and_cache_fp8(const ScatterArgs& a, int src_dtype, float k_scale, float v_scale,
+                                        hipStream_t stream);
 // Copies whole blocks (both pools, every head) for each (src, dst) pair.
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
@@ -71,13 +76,15 @@ hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, in
                                int32_t stride, int32_t* seq_lens, int32_t block_size,
                                hipStream_t stream);
 hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// dtype: the type of q and of the results; kv_fp8: the pools hold FP8 E4M3 codes (else dtype)
 // path: 0 = vector, 1 = MFMA
 // nt: stream the key/value tiles with the non-temporal hint (otherwise ordinary cached loads)
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, int head_dim, int path, bool nt,
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, bool nt,
                               int32_t grid, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.
-hipError_t decode_main_grid_cap(int dtype, int head_dim, int path, int group, int block_size, int32_t* cap);
+hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size,
+                                int32_t* cap);
 
 // ---------------------------------------------------------------- timing hooks
 void timing_before(int kernel, hipStream_t stream);

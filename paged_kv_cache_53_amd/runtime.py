@@ -1,7 +1,9 @@
 """The decode-step runtime around the kernels: device pools + host allocator, and a batch.
 
 PagedKVCache   one layer's key/value pools on the device and the host block allocator that
-               hands out their slots (prompt writes go allocator -> scatter kernel).
+               hands out their slots (prompt writes go allocator -> scatter kernel).  With
+               dtype torch.float8_e4m3fn the pools hold FP8 E4M3 codes under the per-tensor
+               scales k_scale / v_scale (the scatter quantises, decode reads the scaled values).
 DecodeBatch    a fixed set of sequences decoded together: device block tables and lengths,
                a workspace, and ``step()`` -- one decode step of the whole hot path:
                  1. host: the allocator appends one token to every sequence (C++, one call)
@@ -27,13 +29,28 @@ from . import (Allocator, append_slots, copy_blocks, key_pool_shape, paged_atten
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, block_size: int, n_kv_heads: int, head_dim: int, dtype,
-                 device="cuda", free_order: Optional[Sequence[int]] = None, fill: str = "zero"):
+                 device="cuda", free_order: Optional[Sequence[int]] = None, fill: str = "zero",
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None):
         self.num_blocks, self.block_size = num_blocks, block_size
         self.n_kv_heads, self.head_dim, self.dtype, self.device = n_kv_heads, head_dim, dtype, device
+        self.quantised = dtype == torch.float8_e4m3fn
+        if self.quantised != (k_scale is not None and v_scale is not None):
+            raise ValueError("k_scale and v_scale go with (and only with) an FP8 cache")
+        self.scales = {"k_scale": k_scale, "v_scale": v_scale} if self.quantised else {}
         self.allocator = Allocator(num_blocks, block_size, free_order)
         ks = key_pool_shape(num_blocks, n_kv_heads, head_dim, block_size, dtype)
         vs = value_pool_shape(num_blocks, n_kv_heads, head_dim, block_size)
-        if fill == "randn":
+        if self.quantised:
+            code = {"zero": 0x00, "nan": 0x7F}.get(fill)
+            if fill == "randn":
+                self.k_pool = torch.randint(0, 0x7F, ks, device=device, dtype=torch.uint8).view(dtype)
+                self.v_pool = torch.randint(0, 0x7F, vs, device=device, dtype=torch.uint8).view(dtype)
+            elif code is not None:
+                self.k_pool = torch.full(ks, code, device=device, dtype=torch.uint8).view(dtype)
+                self.v_pool = torch.full(vs, code, device=device, dtype=torch.uint8).view(dtype)
+            else:
+                raise ValueError(fill)
+        elif fill == "randn":
             self.k_pool = torch.randn(ks, device=device, dtype=torch.float32).to(dtype)
             self.v_pool = torch.randn(vs, device=device, dtype=torch.float32).to(dtype)
         elif fill == "nan":
@@ -51,7 +68,7 @@ class PagedKVCache:
         self.apply_copies(pairs)
         if slots:
             reshape_and_cache(k, v, torch.tensor(slots, dtype=torch.int64, device=self.device),
-                              self.k_pool, self.v_pool)
+                              self.k_pool, self.v_pool, **self.scales)
 
     def apply_copies(self, pairs) -> None:
         """Makes the private block copies a copy-on-write append asked for (before its scatter)."""
@@ -113,10 +130,10 @@ class DecodeBatch:
         c = self.cache
         c.apply_copies(pairs)   # a forked row writing into a shared block gets its private copy first
         append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
-        reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool)
+        reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool, **c.scales)
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
-                               shared_kv=c.has_shared_blocks())
+                               shared_kv=c.has_shared_blocks(), **c.scales)
         self.steps += 1
 
     def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
@@ -124,4 +141,4 @@ class DecodeBatch:
         c = self.cache
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
-                               shared_kv=c.has_shared_blocks())
+                               shared_kv=c.has_shared_blocks(), **c.scales)

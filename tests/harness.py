@@ -29,10 +29,21 @@ class GpuState:
         import paged_kv_cache_53_amd as pkv
         self.w, self.pkv = w, pkv
         dt = TORCH_DTYPE[w.dtype]
+        fp8 = w.kv_format == "fp8"
+        pdt = torch.float8_e4m3fn if fp8 else dt
+        # an FP8 cache: the scatter quantises under the workload's scales, decode reads them back
+        self.scales = {"k_scale": w.k_scale, "v_scale": w.v_scale} if fp8 else {}
         self.alloc = pkv.Allocator(w.num_blocks, w.block_size, w.free_order.tolist())
-        kshape = pkv.key_pool_shape(w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size, dt)
+        kshape = pkv.key_pool_shape(w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size, pdt)
         vshape = pkv.value_pool_shape(w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size)
-        if poison:
+        if fp8:
+            if poison:    # the NaN code
+                self.k_pool = torch.full(kshape, 0x7F, dtype=torch.uint8, device=device).view(pdt)
+                self.v_pool = torch.full(vshape, 0x7F, dtype=torch.uint8, device=device).view(pdt)
+            else:
+                self.k_pool = torch.randint(0, 0x7F, kshape, dtype=torch.uint8, device=device).view(pdt)
+                self.v_pool = torch.randint(0, 0x7F, vshape, dtype=torch.uint8, device=device).view(pdt)
+        elif poison:
             bits = wl.poison_value(w.dtype)
             ib = torch.int32 if w.dtype == "f32" else torch.int16
             if ib == torch.int16 and bits >= 0x8000:
@@ -48,7 +59,7 @@ class GpuState:
                 assert not pairs
                 k, v = wl.kv_rows(w, op["seq"], op["pos"], op["n"], device=device)
                 sm = torch.tensor(slots, dtype=torch.int64, device=device)
-                pkv.reshape_and_cache(k, v, sm, self.k_pool, self.v_pool)
+                pkv.reshape_and_cache(k, v, sm, self.k_pool, self.v_pool, **self.scales)
                 del k, v
             elif op["op"] == "fork":
                 self.alloc.fork(op["parent"], op["child"], op["n"])
@@ -59,7 +70,7 @@ class GpuState:
         assert not pairs
         self.new_slots = torch.from_numpy(slots.copy()).to(device)
         kn, vn = wl.new_token_kv(w, device=device)
-        pkv.reshape_and_cache(kn, vn, self.new_slots, self.k_pool, self.v_pool)
+        pkv.reshape_and_cache(kn, vn, self.new_slots, self.k_pool, self.v_pool, **self.scales)
         self.stride = int(math.ceil(max(w.max_seq_len, 1) / w.block_size)) + extra_table_cols
         tables, lens = self.alloc.fill_block_tables(w.batch.tolist(), self.stride, pad=table_pad)
         assert np.array_equal(lens, w.seq_lens)
@@ -70,7 +81,7 @@ class GpuState:
         torch.cuda.synchronize()
 
     def decode(self, out_dtype=None, partition_size=None, max_seq_len=None, q=None, workspace=None,
-               shared_kv=False):
+               shared_kv=False, scales=None):
         w = self.w
         odt = TORCH_DTYPE[w.dtype] if out_dtype is None else out_dtype
         q = self.q if q is None else q
@@ -78,12 +89,25 @@ class GpuState:
         self.pkv.paged_attention_decode(out, q, self.k_pool, self.v_pool, self.tables, self.seq_lens,
                                         w.scale, w.max_seq_len if max_seq_len is None else max_seq_len,
                                         w.partition_size if partition_size is None else partition_size,
-                                        workspace=workspace, shared_kv=shared_kv)
+                                        workspace=workspace, shared_kv=shared_kv,
+                                        **(self.scales if scales is None else scales))
         torch.cuda.synchronize()
         return out
 
 
 # ------------------------------------------------------------------------------- oracle side
+def _cached_values(w: wl.Workload, rows_storage, which: str) -> np.ndarray:
+    """fp64 values a cache holds for storage rows of w.dtype: the rows themselves, or for an FP8
+    cache the oracle's dequantised codes of them."""
+    from oracle import attention as O
+    from oracle import fp8 as F
+    x = O.to_f64(wl.storage_to_numpy(rows_storage), w.dtype)
+    if w.kv_format != "fp8":
+        return x
+    s = w.k_scale if which == "k" else w.v_scale
+    return F.dequantize(F.quantize(x.astype(np.float32), s), s)
+
+
 def oracle_rows(w: wl.Workload, rows, q_np=None):
     """Oracle outputs (fp64) for the listed batch rows from their logical K/V (no GPU data)."""
     from oracle import attention as O
@@ -92,24 +116,36 @@ def oracle_rows(w: wl.Workload, rows, q_np=None):
     out = {}
     for r in rows:
         K, V = wl.logical_kv(w, r)
-        out[r] = O.attention_logical(O.to_f64(q_np[r], w.dtype), O.to_f64(wl.storage_to_numpy(K), w.dtype),
-                                     O.to_f64(wl.storage_to_numpy(V), w.dtype), w.scale)
+        out[r] = O.attention_logical(O.to_f64(q_np[r], w.dtype), _cached_values(w, K, "k"),
+                                     _cached_values(w, V, "v"), w.scale)
     return out
 
 
-def oracle_paged(w: wl.Workload):
-    """The oracle's whole paged pipeline: its own allocator, scatter and decode (all rows)."""
+def oracle_paged(w: wl.Workload, with_pools: bool = False):
+    """The oracle's whole paged pipeline: its own allocator, scatter and decode (all rows).
+    Returns (out, allocator model, tables), and the oracle's pools too when with_pools."""
     from oracle import attention as O
     from oracle import scatter as SC
     from oracle.allocator import BlockAllocatorModel
-    st = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    fp8 = w.kv_format == "fp8"
+    st = np.uint8 if fp8 else {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
     a = BlockAllocatorModel(w.num_blocks, w.block_size, w.free_order)
-    kp, vp = SC.empty_pools(w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size, st, wl.poison_value(w.dtype))
+    kp, vp = SC.empty_pools(w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size, st,
+                            0x7F if fp8 else wl.poison_value(w.dtype))
+
+    def scatter(k, v, slots):
+        if fp8:   # the rows' exact fp32 values, quantised by the oracle's scatter
+            kf = O.to_f64(wl.storage_to_numpy(k), w.dtype).astype(np.float32)
+            vf = O.to_f64(wl.storage_to_numpy(v), w.dtype).astype(np.float32)
+            SC.reshape_and_cache_fp8(kf, vf, slots, kp, vp, w.k_scale, w.v_scale)
+        else:
+            SC.reshape_and_cache(wl.storage_to_numpy(k), wl.storage_to_numpy(v), slots, kp, vp)
+
     for op in w.prompt_ops:
         if op["op"] == "alloc":
             slots, _ = a.alloc(op["seq"], op["n"])
             k, v = wl.kv_rows(w, op["seq"], op["pos"], op["n"])
-            SC.reshape_and_cache(wl.storage_to_numpy(k), wl.storage_to_numpy(v), np.array(slots), kp, vp)
+            scatter(k, v, np.array(slots))
         elif op["op"] == "fork":
             a.fork(op["parent"], op["child"], op["n"])
         else:
@@ -118,15 +154,18 @@ def oracle_paged(w: wl.Workload):
     for seq in w.batch.tolist():
         new += a.alloc(seq, 1)[0]
     kn, vn = wl.new_token_kv(w)
-    SC.reshape_and_cache(wl.storage_to_numpy(kn), wl.storage_to_numpy(vn), np.array(new), kp, vp)
+    scatter(kn, vn, np.array(new))
     maxb = max(1, max(len(a.block_table(int(s))) for s in w.batch))
     tables = np.zeros((w.num_seqs, maxb), dtype=np.int64)
     for r, seq in enumerate(w.batch.tolist()):
         t = a.block_table(seq)
         tables[r, :len(t)] = t
     q = wl.storage_to_numpy(wl.q_values(w))
-    out = O.paged_attention_decode(q, kp, vp, tables, w.seq_lens, w.scale, w.dtype)
-    return out, a, tables
+    if fp8:
+        out = O.paged_attention_decode_fp8(q, w.dtype, kp, vp, w.k_scale, w.v_scale, tables, w.seq_lens, w.scale)
+    else:
+        out = O.paged_attention_decode(q, kp, vp, tables, w.seq_lens, w.scale, w.dtype)
+    return (out, a, tables, kp, vp) if with_pools else (out, a, tables)
 
 
 def max_abs_err(gpu_out: torch.Tensor, ref: np.ndarray, rows=None) -> float:

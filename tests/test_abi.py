@@ -43,6 +43,9 @@ def test_pool_bytes():
     assert lib.pkv_pool_bytes(64, 4, 64, 16, pkv.PKV_F32) == 64 * 4 * 64 * 16 * 4
     assert lib.pkv_pool_bytes(64, 4, 60, 16, pkv.PKV_F16) == 0     # head_dim not a multiple of 8
     assert lib.pkv_pool_bytes(0, 4, 64, 16, pkv.PKV_F32) == 0
+    assert lib.pkv_pool_bytes(100, 8, 128, 16, pkv.PKV_FP8_E4M3) == 100 * 8 * 128 * 16
+    assert lib.pkv_pool_bytes(100, 8, 120, 16, pkv.PKV_FP8_E4M3) == 0   # 16 codes per key vector
+    assert lib.pkv_pool_bytes(100, 8, 128, 16, 4) == 0                   # no such type
 
 
 def test_workspace_size_is_monotone_and_covers_partials():
@@ -108,6 +111,63 @@ def test_scatter_and_append_reject_bad_arguments():
     assert c(None, 16, 16, 1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID
     assert c(16, 16, 18, 1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID             # misaligned pairs
     assert c(None, None, None, 0, 10, 2, 128, 16, F16, None) == pkv.PKV_OK               # nothing to copy
+
+
+def test_fp8_entries_reject_bad_arguments_before_launch():
+    lib = pkv.lib()
+    BF16, F16, FP8 = pkv.PKV_BF16, pkv.PKV_F16, pkv.PKV_FP8_E4M3
+    f = lib.pkv_reshape_and_cache_fp8
+
+    def scat(**kw):
+        a = dict(k=16, v=16, sm=16, T=4, ks=0, vs=0, kp=16, vp=16, N=10, Hk=2, D=128, B=16, dt=BF16,
+                 kscale=0.01, vscale=0.02)
+        a.update(kw)
+        return f(a["k"], a["v"], a["sm"], a["T"], a["ks"], a["vs"], a["kp"], a["vp"], a["N"], a["Hk"], a["D"],
+                 a["B"], a["dt"], a["kscale"], a["vscale"], None)
+
+    assert scat(T=0) == pkv.PKV_OK                                      # empty: no launch
+    assert scat(dt=FP8) == pkv.PKV_ERR_INVALID                          # sources are never codes
+    assert scat(dt=7) == pkv.PKV_ERR_INVALID
+    assert scat(D=120) == pkv.PKV_ERR_INVALID                           # 16 codes per key vector
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert scat(kscale=bad) == pkv.PKV_ERR_INVALID
+        assert scat(vscale=bad) == pkv.PKV_ERR_INVALID
+    assert scat(k=None) == pkv.PKV_ERR_INVALID
+    assert scat(kp=24) == pkv.PKV_ERR_INVALID                           # misaligned pool
+    assert scat(ks=260) == pkv.PKV_ERR_INVALID                          # row stride of 520 B
+    # the 16-bit scatter does not take FP8 pools: quantising needs the scales
+    assert lib.pkv_reshape_and_cache(16, 16, 16, 4, 0, 0, 16, 16, 10, 2, 128, 16, FP8, None) == pkv.PKV_ERR_INVALID
+
+    d = lib.pkv_paged_attention_decode_fp8
+
+    def dec(**kw):
+        a = dict(out=16, out_dtype=BF16, q=16, qdt=BF16, k=16, v=16, kscale=0.01, vscale=0.02, bt=16, stride=8,
+                 lens=16, S=2, Hq=8, Hk=2, D=128, B=16, N=100, scale=0.1, maxL=128, P=512, ws=256, wsb=1 << 30,
+                 flags=0)
+        a.update(kw)
+        return d(a["out"], a["out_dtype"], a["q"], a["qdt"], a["k"], a["v"], a["kscale"], a["vscale"], a["bt"],
+                 a["stride"], a["lens"], a["S"], a["Hq"], a["Hk"], a["D"], a["B"], a["N"], a["scale"], a["maxL"],
+                 a["P"], a["ws"], a["wsb"], a["flags"], None)
+
+    assert dec(S=0) == pkv.PKV_OK
+    assert dec(qdt=pkv.PKV_F32, out_dtype=pkv.PKV_F32) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(qdt=FP8, out_dtype=FP8) == pkv.PKV_ERR_INVALID          # q is never FP8
+    assert dec(out_dtype=F16) == pkv.PKV_ERR_INVALID                    # out: q's type or fp32
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert dec(kscale=bad) == pkv.PKV_ERR_INVALID
+        assert dec(vscale=bad) == pkv.PKV_ERR_INVALID
+    assert dec(flags=2) == pkv.PKV_ERR_INVALID
+    assert dec(Hq=34, Hk=2) == pkv.PKV_ERR_UNSUPPORTED                  # group 17
+    assert dec(D=96) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(q=None) == pkv.PKV_ERR_INVALID
+    assert dec(wsb=1024) == pkv.PKV_ERR_INVALID
+    # the 16-bit entry does not read FP8 pools
+    assert lib.pkv_paged_attention_decode_ex(16, FP8, 16, 16, 16, 16, 8, 16, 1, 8, 2, 128, 16, 100, 0.1, 128,
+                                             512, 256, 1 << 30, FP8, 0, None) == pkv.PKV_ERR_INVALID
+    # FP8 pools copy like any other: only the byte count matters
+    assert lib.pkv_copy_blocks(16, 16, 16, -1, 10, 2, 128, 16, FP8, None) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_copy_blocks(None, None, None, 0, 10, 2, 128, 16, FP8, None) == pkv.PKV_OK
+    assert lib.pkv_copy_blocks(16, 16, 16, 1, 10, 1, 8, 1, FP8, None) == pkv.PKV_ERR_UNSUPPORTED   # 8-byte blocks
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

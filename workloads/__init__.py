@@ -32,7 +32,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 __all__ = [
-    "Workload", "build", "CONFIG_NAMES", "DTYPE_BYTES", "kv_rows", "q_values",
+    "Workload", "build", "quantised", "CONFIG_NAMES", "DTYPE_BYTES", "kv_rows", "q_values",
     "logical_kv", "storage_to_numpy", "normal_table", "poison_value",
 ]
 
@@ -84,6 +84,9 @@ class Workload:
     partition_size: int = 512
     placement: str = "random"
     variant: str = "full"
+    kv_format: str = "native"       # "native": pools of ``dtype``; "fp8": E4M3 codes of the rows
+    k_scale: float = 1.0            # per-tensor scales of an "fp8" cache (code of x / scale)
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -105,13 +108,19 @@ class Workload:
     def esize(self) -> int:
         return DTYPE_BYTES[self.dtype]
 
+    @property
+    def kv_esize(self) -> int:
+        """Bytes of one cached element (1 for an FP8 cache)."""
+        return 1 if self.kv_format == "fp8" else self.esize
+
     def describe(self) -> dict:
         return {
             "workload": self.name, "variant": self.variant, "seqs": self.num_seqs,
             "n_q_heads": self.n_q_heads, "n_kv_heads": self.n_kv_heads,
             "head_dim": self.head_dim, "block_size": self.block_size, "dtype": self.dtype,
             "num_blocks": self.num_blocks, "placement": self.placement,
-            "partition_size": self.partition_size, "seed": self.seed,
+            "partition_size": self.partition_size, "seed": self.seed, "kv_format": self.kv_format,
+            **({"k_scale": self.k_scale, "v_scale": self.v_scale} if self.kv_format == "fp8" else {}),
             "total_tokens": int(self.seq_lens.sum()), "max_seq_len": self.max_seq_len,
         }
 
@@ -249,6 +258,19 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
                             placement, variant, partition_size or 2048)
 
     raise ValueError(f"unknown config {config_id}")
+
+
+# Scales of the quantised variants: the rows are N(0, 1) draws whose largest magnitude is 4.32
+# (the table's extreme quantile), so x / 0.01 stays below the format's 448 and no element
+# saturates (tests that need saturation pick smaller scales); the two pools get different scales.
+FP8_K_SCALE, FP8_V_SCALE = 0.01, 0.0125
+
+
+def quantised(w: Workload, k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE) -> Workload:
+    """The same workload with an FP8 E4M3 cache: rows of ``w.dtype`` (which q and the results
+    keep) are stored as the codes of x / k_scale and x / v_scale."""
+    return dataclasses.replace(w, kv_format="fp8", k_scale=float(k_scale), v_scale=float(v_scale),
+                               variant=w.variant + "-fp8")
 
 
 def custom(*, seed: int, lens, n_q_heads: int, n_kv_heads: int, head_dim: int,
