@@ -14,7 +14,7 @@
 //   of single-wave workgroups takes units from one atomic counter, so no wave is
 //   launched for a partition that does not exist and long and short rows balance
 //   across the 256 CUs.
-// * A wave streams its units in 16-token tiles through three register buffers,
+// * A wave streams its units in tiles (16 tokens; 32 for an FP8 cache) through three register buffers,
 //   two tiles in flight: while tile t is computed, tiles t+1 and t+2 are loading.
 //   The issue side runs ahead across unit boundaries (it claims the next unit a
 //   few tiles before the current one ends and loads that unit's q), so HBM sees
@@ -39,8 +39,10 @@
 //   or f16): the same MFMA products after widening the codes in registers to
 //   q's type, which holds every E4M3 value exactly.  A key vector is 16 codes
 //   (16 bytes), so a lane's q fragments take the matching dims; the key scale
-//   is folded into the score scale and the value scale into the output.  The
-//   tile's bytes halve, its loads stay the same in number.
+//   is folded into the score scale and the value scale into the output.  Its
+//   tiles hold 32 tokens, so that a tile has the bytes and the load widths of
+//   a 16-bit one (the QK rows are ordered so that the scores land in the
+//   operand layout of a 32-deep PV MFMA).
 // * Vector path (fp32 KV): per-token dot products with a 4-lane
 //   cross-group reduction, fp32 weights, FMA accumulation.
 // * q fragments live in LDS (one slot for the unit being computed, one for the
@@ -276,18 +278,6 @@ template <> struct Kv<_Float16> { static constexpr int X = 8; using VV = u32x2; 
 template <> struct Kv<float> { static constexpr int X = 4; using VV = u32x4; };
 template <> struct Kv<E4M3> { static constexpr int X = 16; using VV = unsigned; };
 
-// Register-resident tile of 16 tokens.  Keys: lane (token lane%16, group g = lane/16) holds
-// the 16-byte vectors 4ks+g of its token's row (the A operand of the MFMA QK product, and the
-// vector path's share of the dot product).  Values: lane (dim 16dt + lane%16, group g) holds
-// tokens 4g..4g+3 of that dim (the A operand of the MFMA PV product).
-template <typename T, int D>
-struct Tile16 {
-  static constexpr int NK = D / Kv<T>::X / 4;
-  static constexpr int kLoads = NK + D / 16;   // vector-memory instructions per tile
-  u32x4 kf[NK];
-  typename Kv<T>::VV vf[D / 16];
-};
-
 // One work unit (row s, KV head kvh, partition part); all fields are wave-uniform.
 template <typename T>
 struct Unit {
@@ -316,38 +306,118 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   return u;
 }
 
-// Issues the Tile16::kLoads loads of the 16-token tile at partition offset t0 of a unit (block
-// table row bt, ntok tokens, pools offset to its KV head), completion explicitly waited when E
-// (vload).  Block ids are wave-uniform scalar loads (the first one was read when the unit was
-// opened); table entries past the unit's last block are never read (those tokens reuse the
-// first id and are masked in the compute).
-template <typename T, int D, int Bsz, bool E, bool NT>
-__device__ inline void issue_tile(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok,
-                                  const T* kbase, const T* vbase, int t0, int64_t blk_stride,
-                                  Tile16<T, D>& R) {
-  constexpr int X = Kv<T>::X;
-  using VV = typename Kv<T>::VV;
-  constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
-  const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
-  const int first = t0 / Bsz;
-  int id0 = first == 0 ? id_first : ld_uniform(bt, first);
-  id0 = min(max(id0, 0), a.num_blocks - 1);
-  int id1 = id0;
-  if constexpr (NB == 2) {
-    if (t0 + 8 < ntok) {
-      id1 = ld_uniform(bt, first + 1);
-      id1 = min(max(id1, 0), a.num_blocks - 1);
+// Register-resident tile of 16 tokens.  Keys: lane (token lane%16, group g = lane/16) holds
+// the 16-byte vectors 4ks+g of its token's row (the A operand of the MFMA QK product, and the
+// vector path's share of the dot product).  Values: lane (dim 16dt + lane%16, group g) holds
+// tokens 4g..4g+3 of that dim (the A operand of the MFMA PV product).
+template <typename T, int D>
+struct Tile16 {
+  static constexpr int kTokens = 16;
+  static constexpr int NK = D / Kv<T>::X / 4;
+  static constexpr int kLoads = NK + D / 16;   // vector-memory instructions per tile
+  u32x4 kf[NK];
+  typename Kv<T>::VV vf[D / 16];
+
+  // Issues the kLoads loads of the tile at partition offset t0 of a unit (block table row bt,
+  // ntok tokens, pools offset to its KV head), completion explicitly waited when E (vload).
+  // Block ids are wave-uniform scalar loads (the first one was read when the unit was opened);
+  // table entries past the unit's last block are never read (those tokens reuse the first id
+  // and are masked in the compute).
+  template <int Bsz, bool E, bool NT>
+  __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const T* kbase,
+                        const T* vbase, int t0, int64_t blk_stride) {
+    constexpr int X = Kv<T>::X;
+    constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int first = t0 / Bsz;
+    int id0 = first == 0 ? id_first : ld_uniform(bt, first);
+    id0 = min(max(id0, 0), a.num_blocks - 1);
+    int id1 = id0;
+    if constexpr (NB == 2) {
+      if (t0 + 8 < ntok) {
+        id1 = ld_uniform(bt, first + 1);
+        id1 = min(max(id1, 0), a.num_blocks - 1);
+      }
     }
+    const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
+    const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[ks], kb + ks * 4 * Bsz * X);
+    const int bv = (NB == 2 && g >= 2) ? id1 : id0;
+    const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
   }
-  const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
-  const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
+  // orders every later use of the tile's registers after the preceding wait
+  template <bool E> __device__ void tie_all() {
 #pragma unroll
-  for (int ks = 0; ks < Tile16<T, D>::NK; ++ks) vload<E, NT>(R.kf[ks], kb + ks * 4 * Bsz * X);
-  const int bv = (NB == 2 && g >= 2) ? id1 : id0;
-  const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
+    for (int ks = 0; ks < NK; ++ks) tie<E>(kf[ks]);
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(R.vf[dt], vb + dt * 16 * Bsz);
-}
+    for (int dt = 0; dt < D / 16; ++dt) tie<E>(vf[dt]);
+  }
+};
+
+// Register-resident tile of 32 tokens of an FP8 cache: the same bytes per tile and the same
+// load widths as a 16-token tile of 16-bit KV.  The QK product runs as two 16-row MFMA blocks;
+// row r of block b is token 8(r/4) + 4b + r%4, so the two accumulators give lane (head, g) the
+// scores of tokens 8g..8g+7 -- exactly the B operand of one 32-deep PV MFMA, whose A operand is
+// then 8 consecutive codes of one value dim (one 8-byte load).
+//   kf[b][ks]: lane (row r16, g) holds 16-code key vector 4ks+g of token 8(r16/4) + 4b + r16%4
+//   vf[dt]:    lane (dim 16dt + r16, g) holds the codes of tokens 8g..8g+7
+template <int D>
+struct Tile32F8 {
+  static constexpr int kTokens = 32;
+  static constexpr int NK = D / 64;            // key vectors per lane and row block
+  static constexpr int kLoads = 2 * NK + D / 16;
+  u32x4 kf[2][NK];
+  u32x2 vf[D / 16];
+
+  template <int Bsz, bool E, bool NT>
+  __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const E4M3* kbase,
+                        const E4M3* vbase, int t0, int64_t blk_stride) {
+    constexpr int NB = 32 / Bsz;                 // blocks per tile: 4, 2 or 1
+    constexpr int TPB = Bsz / 8;                 // 8-token groups per block
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int first = t0 / Bsz;
+    int id[NB];
+    id[0] = first == 0 ? id_first : ld_uniform(bt, first);
+#pragma unroll
+    for (int j = 1; j < NB; ++j) {
+      id[j] = id[0];
+      if (t0 + j * Bsz < ntok) id[j] = ld_uniform(bt, first + j);   // later blocks of the tile, if any token is real
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) id[j] = min(max(id[j], 0), a.num_blocks - 1);
+    // key rows: token 8(r16/4) + 4b + r16%4 lies in block (r16/4) / TPB of the tile
+    const int jk = (r16 >> 2) / TPB;
+    int bk = id[0];
+#pragma unroll
+    for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int tok = (8 * (r16 >> 2) + 4 * b + (r16 & 3)) & (Bsz - 1);
+      const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + tok) * 16;
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[b][ks], kb + ks * 4 * Bsz * 16);
+    }
+    // value dims: tokens 8g..8g+7 lie in block g / TPB
+    const int jv = g / TPB;
+    int bv = id[0];
+#pragma unroll
+    for (int j = 1; j < NB; ++j) bv = jv == j ? id[j] : bv;
+    const E4M3* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((8 * g) & (Bsz - 1));
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
+  }
+  template <bool E> __device__ void tie_all() {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) tie<E>(kf[b][ks]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) tie<E>(vf[dt]);
+  }
+};
 
 // q fragments of one query head hq of row s (q of type T, keys stored as KV): lane (r16, g)
 // holds, in D / XQ / 4 16-byte vectors of XQ elements, the dims of the key vectors 4k+g its
@@ -444,7 +514,7 @@ struct MfmaMath {
   static constexpr int NQ = D / 32;       // q vectors per lane: one per 32-wide MFMA k-step
   static constexpr bool kPrefetchQ = true;
   static constexpr bool kQuant = !std::is_same<KV, T>::value;
-  using Tile = Tile16<KV, D>;
+  using Tile = typename std::conditional<kQuant, Tile32F8<D>, Tile16<KV, D>>::type;
   f32x4 acc[D / 16];
   float m_run, l_run;
 
@@ -461,6 +531,11 @@ struct MfmaMath {
     load_q_head<T, KV, D, kAsync>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
   }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
+    if constexpr (kQuant) compute32(R, q_lds, t0, ntok, scale_log2);
+    else compute16(R, q_lds, t0, ntok, scale_log2);
+  }
+  // 16 tokens of 16-bit KV: S^T with one 16x16x32 MFMA per 32 dims, O^T += V^T P^T with 16x16x16
+  __device__ void compute16(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     using V8 = typename Vec8<T>::type;
     const int g = threadIdx.x >> 4;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -469,12 +544,7 @@ struct MfmaMath {
       const u32x4 qb = q_lds[0][j][threadIdx.x];
       V8 qv, kv;
       __builtin_memcpy(&qv, &qb, 16);
-      if constexpr (kQuant) {   // key vector j / 2 holds 16 codes: q vector j takes half j % 2
-        const u32x4 kw = R.kf[j / 2];
-        kv = (j % 2) ? widen8<T>(kw[2], kw[3]) : widen8<T>(kw[0], kw[1]);
-      } else {
-        __builtin_memcpy(&kv, &R.kf[j], 16);
-      }
+      __builtin_memcpy(&kv, &R.kf[j], 16);
       sc = mfma_16x16x32(kv, qv, sc);
     }
     float x[4];
@@ -504,9 +574,7 @@ struct MfmaMath {
     __builtin_memcpy(&pb, pt, 8);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 va;
-      if constexpr (kQuant) va = widen4(R.vf[dt], T{});
-      else va = R.vf[dt];
+      u32x2 va = R.vf[dt];
       if (partial) {
         T vt[4];
         __builtin_memcpy(vt, &va, 8);
@@ -516,6 +584,66 @@ struct MfmaMath {
         __builtin_memcpy(&va, vt, 8);
       }
       acc[dt] = mfma_16x16x16(va, pb, acc[dt] * alpha, T{});
+    }
+  }
+  // 32 tokens of FP8 codes widened to T: two 16-row QK blocks per 32 dims, then one 32-deep
+  // PV MFMA per 16 dims.  Lane (head r16, g) ends the QK product with the scores of tokens
+  // 8g..8g+7 (block 0 rows 4g..4g+3 are tokens 8g..8g+3, block 1 rows are tokens 8g+4..8g+7).
+  __device__ void compute32(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
+    using V8 = typename Vec8<T>::type;
+    const int g = threadIdx.x >> 4;
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {   // key vector j / 2 holds 16 codes: q vector j takes half j % 2
+      const u32x4 qb = q_lds[0][j][threadIdx.x];
+      V8 qv;
+      __builtin_memcpy(&qv, &qb, 16);
+      const u32x4 k0 = R.kf[0][j / 2], k1 = R.kf[1][j / 2];
+      const V8 a0 = (j % 2) ? widen8<T>(k0[2], k0[3]) : widen8<T>(k0[0], k0[1]);
+      const V8 a1 = (j % 2) ? widen8<T>(k1[2], k1[3]) : widen8<T>(k1[0], k1[1]);
+      s0 = mfma_16x16x32(a0, qv, s0);
+      s1 = mfma_16x16x32(a1, qv, s1);
+    }
+    float x[8];   // token 8g + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = s0[i] * scale_log2;
+      x[4 + i] = s1[i] * scale_log2;
+    }
+    const bool partial = t0 + 32 > ntok;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (t0 + 8 * g + i >= ntok) x[i] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mt = fmaxf(mt, xor_f(mt, 16));
+    mt = fmaxf(mt, xor_f(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    T pt[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pt[i] = static_cast<T>(fast_exp2(x[i] - m_new));
+      psum += to_f32(pt[i]);
+    }
+    l_run = l_run * alpha + psum;
+    V8 pb;
+    __builtin_memcpy(&pb, pt, 16);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      V8 va = widen8<T>(R.vf[dt][0], R.vf[dt][1]);
+      if (partial) {
+        T vt[8];
+        __builtin_memcpy(vt, &va, 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (t0 + 8 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
+        __builtin_memcpy(&va, vt, 16);
+      }
+      acc[dt] = mfma_16x16x32(va, pb, acc[dt] * alpha);
     }
   }
   // the normalised output when the row has one partition, else (max, sum, accumulator); with
@@ -684,7 +812,7 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
       : "v"(a.counters + 1), "v"(1));
 }
 
-// Persistent wave over a stream of 16-token tiles of the units it claims, with the loads of
+// Persistent wave over a stream of tiles of the units it claims, with the loads of
 // the tile two steps ahead in flight while the current tile is computed (three tile buffers
 // in rotation).  The issue side runs up to one unit ahead of the compute side.  With
 // kPrefetchQ it loads that unit's q into registers before the unit's first tile loads and
@@ -698,7 +826,8 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
 template <typename KV, int D, int Bsz, class Math, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
-  using Tile = Tile16<KV, D>;
+  using Tile = typename Math::Tile;
+  constexpr int TT = Tile::kTokens;   // tokens per tile
   constexpr int NQ = Math::NQ;
   // explicitly waited loads while three tiles fit in 96 registers (32 per tile)
   constexpr bool E = sizeof(Tile) <= 32 * 4;
@@ -783,7 +912,7 @@ void decode_kernel(DecodeArgs a) {
     }
     const bool is_real = ti < ui.ntok;
     // the claim goes before this step's tile loads, so they count towards its wait
-    if (is_real && !(fl & (kClaimed | kNext | kEnded)) && ui.ntok - (ti + 16) <= kClaimAhead * 16) {
+    if (is_real && !(fl & (kClaimed | kNext | kEnded)) && ui.ntok - (ti + TT) <= kClaimAhead * TT) {
       claim_unit<E>(a, pending);
       fl |= kClaimed;
     }
@@ -792,11 +921,11 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    issue_tile<KV, D, Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
-                             is_real ? +ui.ntok : +uc.ntok,
-                             is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
-                             is_real ? +ti : tc_now, blk_stride, Y);
-    ti += is_real ? 16 : 0;   // a select: a conditional update would put ti in memory
+    Y.template issue<Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+                                 is_real ? +ui.ntok : +uc.ntok,
+                                 is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
+                                 is_real ? +ti : tc_now, blk_stride);
+    ti += is_real ? TT : 0;   // a select: a conditional update would put ti in memory
     return is_real;
   };
 
@@ -829,13 +958,10 @@ void decode_kernel(DecodeArgs a) {
     real = issue_next(Y, tc) ? (real | YB) : (real & ~YB);
     // X was issued two steps ago; each of the two steps since issued LT tile loads
     vm_wait<E, 2 * LT>();
-#pragma unroll
-    for (int ks = 0; ks < Tile::NK; ++ks) tie<E>(X.kf[ks]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) tie<E>(X.vf[dt]);
+    X.template tie_all<E>();
     if (!x_real) return true;   // a filler: nothing to compute this step
     mt.compute(X, q_lds[slot_c], tc, uc.ntok, scale_log2);
-    tc += 16;
+    tc += TT;
     if (tc < uc.ntok) return true;
     mt.finish(a, uc);
     if (!(fl & kAhead)) return false;   // the issue side found no further unit: every issued tile is filler
