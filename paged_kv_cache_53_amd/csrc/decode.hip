@@ -345,8 +345,13 @@ struct Tile16 {
     for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[ks], kb + ks * 4 * Bsz * X);
     const int bv = (NB == 2 && g >= 2) ? id1 : id0;
     const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
+    // A block of more than 16 tokens holds each value dim's tokens in a row longer than the tile's
+    // share: the tile reads half of every line and the next tile the other half, so those lines
+    // stay cacheable (the non-temporal hint made the second half come from HBM again: 1115 us
+    // instead of 840 us on the Llama-70B-class batch at B = 32).  Key lines are read whole.
+    constexpr bool kNTV = NT && Bsz <= 16;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
+    for (int dt = 0; dt < D / 16; ++dt) vload<E, kNTV>(vf[dt], vb + dt * 16 * Bsz);
   }
   // orders every later use of the tile's registers after the preceding wait
   template <bool E> __device__ void tie_all() {
