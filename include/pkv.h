@@ -243,6 +243,77 @@ int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int 
                                    int32_t partition_size, void* workspace, size_t workspace_bytes,
                                    uint32_t flags, void* stream);
 
+/* ---- flat spans: contiguous virtual ranges backed on demand ------------------------------
+ * The alternative to a block table that "Contiguous vs Paged KV Cache on RDNA4" names (sections
+ * "Is paging the only way to fix KV cache fragmentation?" and "Why the single-user verdict
+ * flipped"): every sequence gets one contiguous virtual range reserved up front, physical memory
+ * is mapped into it as the sequence grows, and attention reads the range as a flat span with no
+ * block table.
+ *
+ * A span pool reserves one virtual range per pool (keys, values) and cuts it into max_spans
+ * spans.  A span keeps the documented block layout: span s holds blocks s * blocks_per_span ..
+ * (s + 1) * blocks_per_span - 1 of a virtual pool of num_blocks = max_spans * blocks_per_span
+ * blocks, so token p of span s has slot (s * blocks_per_span + p / B) * B + p % B and
+ * pkv_reshape_and_cache / pkv_copy_blocks work on it unchanged (k_base / v_base as the pools).
+ * Physical memory comes in chunks of chunk_bytes (0 = 2 MiB; a multiple of the device's allocation
+ * granularity), mapped with the HIP virtual memory API.  Only mapped memory may be touched: every
+ * slot written and every token a decode reads must lie in a reserved prefix of its span (reading
+ * or writing an unmapped part of a span is a GPU memory fault).  A released span's chunks are kept
+ * for reuse until pkv_span_pool_trim.  The pool belongs to the device current at creation; it is
+ * not thread-safe across threads that also launch on its memory without synchronising. */
+typedef struct pkv_span_pool pkv_span_pool;
+
+typedef struct {
+  void* k_base;             /* device: the key pool's virtual range */
+  void* v_base;             /* device: the value pool's virtual range */
+  int32_t blocks_per_span;
+  int32_t num_blocks;       /* max_spans * blocks_per_span */
+  size_t chunk_bytes;
+  size_t span_bytes;        /* one span of one pool: blocks_per_span * block bytes */
+  size_t mapped_bytes;      /* physical memory mapped now, both pools */
+  size_t spare_bytes;       /* unmapped chunks kept for reuse */
+} pkv_span_info;
+
+/* max_tokens: the longest sequence a span must hold (blocks_per_span >= ceil(max_tokens / B); it
+ * is rounded up so that a span is a whole number of chunks).  dtype: any pool type.
+ * PKV_ERR_UNSUPPORTED if the device has no virtual memory management; PKV_ERR_OOM if the virtual
+ * ranges cannot be reserved. */
+int pkv_span_pool_create(int32_t max_spans, int32_t max_tokens, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t block_size, int dtype, size_t chunk_bytes, pkv_span_pool** out);
+void pkv_span_pool_destroy(pkv_span_pool* p);
+
+/* Backs tokens [0, n_tokens) of span (in both pools) with physical memory: maps the missing chunks.
+ * All or nothing: PKV_ERR_OOM (no device memory) or PKV_ERR_HIP leaves the span as it was.
+ * n_tokens above the span's capacity: PKV_ERR_INVALID.  Never shrinks a span. */
+int pkv_span_reserve(pkv_span_pool* p, int32_t span, int32_t n_tokens);
+
+/* Unmaps all of a span's memory (its contents are lost); the chunks are kept for reuse.  Work on the
+ * device that still reads or writes the span must have finished. */
+int pkv_span_release(pkv_span_pool* p, int32_t span);
+
+/* Frees the chunks kept for reuse. */
+int pkv_span_pool_trim(pkv_span_pool* p);
+
+int pkv_span_pool_info(pkv_span_pool* p, pkv_span_info* out);
+
+/* Tokens of span that are backed now (a multiple of B), or -1 for a bad argument. */
+int32_t pkv_span_mapped_tokens(pkv_span_pool* p, int32_t span);
+
+/* Decode attention over flat spans: pkv_paged_attention_decode_ex where row s's token j is token
+ * j % B of block span_ids[s] * blocks_per_span + j / B, computed in the kernel (no block table is
+ * read).  k_base / v_base, num_blocks and blocks_per_span come from pkv_span_pool_info;
+ * span_ids is device int32 [num_seqs].  Every row's first seq_lens[s] tokens must be reserved.
+ * max_seq_len must fit a span (ceil(max_seq_len / B) <= blocks_per_span).  16-bit KV only
+ * (PKV_ERR_UNSUPPORTED for fp32), and PKV_DECODE_SHARED_KV is unsupported (spans are never
+ * shared).  The result is bit-identical to pkv_paged_attention_decode_ex over the same tokens. */
+int pkv_paged_attention_decode_flat(void* out, int out_dtype, const void* q, const void* k_base,
+                                    const void* v_base, const int32_t* span_ids, int32_t blocks_per_span,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, float scale, int32_t max_seq_len,
+                                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                    int kv_dtype, uint32_t flags, void* stream);
+
 /* ---- host block allocator ------------------------------------------------------
  * The block manager of the pages: a free list of physical block ids, a
  * reference count per block, and per-sequence block tables.

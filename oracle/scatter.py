@@ -105,3 +105,17 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> None:
             continue
         k_pool[dst] = k_pool[src]
         v_pool[dst] = v_pool[src]
+
+
+def flat_span_table(span: int, blocks_per_span: int, L: int, B: int):
+    """The blocks a flat span gives a sequence of L tokens: logical block i is block
+    span * blocks_per_span + i of one virtual pool ("Contiguous vs Paged KV Cache on RDNA4", sections
+    "Is paging the only way to fix KV cache fragmentation?" and "Why the single-user verdict flipped": a
+    sequence gets one contiguous virtual range reserved up front and physical memory committed into it on
+    demand, so reading it needs no block table).  Cut into blocks of the pools' layout, that range is the
+    consecutive blocks of the sequence's span; token p then sits at slot
+    (span * blocks_per_span + p // B) * B + p % B."""
+    nb = -(-L // B)
+    if nb > blocks_per_span:
+        raise ValueError("sequence longer than its span")
+    return [span * blocks_per_span + i for i in range(nb)]

@@ -25,7 +25,8 @@ from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PK
 __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
-    "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks",
+    "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
+    "reshape_and_cache_spans", "paged_attention_decode_flat",
 ]
 
 
@@ -202,6 +203,91 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
         dtype_code(k_pool), flags, _stream(stream)),
         "pkv_paged_attention_decode_ex")
+
+
+class SpanPool:
+    """Flat spans (pkv_span_pool): one contiguous virtual range per sequence, physical memory mapped
+    on demand in chunks.  Span s holds blocks s * blocks_per_span .. of a virtual pool in the
+    documented layout; token p of span s has slot (s * blocks_per_span + p // B) * B + p % B."""
+
+    def __init__(self, max_spans: int, max_tokens: int, n_kv_heads: int, head_dim: int, block_size: int, dtype,
+                 chunk_bytes: int = 0):
+        self._h = C.c_void_p()
+        _check(lib().pkv_span_pool_create(max_spans, max_tokens, n_kv_heads, head_dim, block_size,
+                                          dtype_code(dtype), chunk_bytes, C.byref(self._h)), "pkv_span_pool_create")
+        self.max_spans, self.block_size, self.n_kv_heads, self.head_dim = max_spans, block_size, n_kv_heads, head_dim
+        self.dtype = dtype
+        inf = self.info()
+        self.k_base, self.v_base = inf["k_base"], inf["v_base"]
+        self.blocks_per_span, self.num_blocks = inf["blocks_per_span"], inf["num_blocks"]
+        self.chunk_bytes = inf["chunk_bytes"]
+
+    def info(self) -> dict:
+        st = _lib.pkv_span_info()
+        _check(lib().pkv_span_pool_info(self._h, C.byref(st)), "pkv_span_pool_info")
+        return {name: getattr(st, name) for name, _ in st._fields_}
+
+    def reserve(self, span: int, n_tokens: int) -> None:
+        _check(lib().pkv_span_reserve(self._h, span, n_tokens), "pkv_span_reserve")
+
+    def release(self, span: int) -> None:
+        _check(lib().pkv_span_release(self._h, span), "pkv_span_release")
+
+    def trim(self) -> None:
+        _check(lib().pkv_span_pool_trim(self._h), "pkv_span_pool_trim")
+
+    def mapped_tokens(self, span: int) -> int:
+        return int(lib().pkv_span_mapped_tokens(self._h, span))
+
+    def slot(self, span: int, pos: int) -> int:
+        B = self.block_size
+        return (span * self.blocks_per_span + pos // B) * B + pos % B
+
+    def close(self) -> None:
+        if self._h:
+            lib().pkv_span_pool_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def reshape_and_cache_spans(k, v, slot_mapping, pool: SpanPool, stream=None) -> None:
+    """pkv_reshape_and_cache into a span pool's virtual pools (the slots must be reserved)."""
+    T = k.shape[0]
+    Hk, D = pool.n_kv_heads, pool.head_dim
+    if k.shape != (T, Hk, D) or v.shape != (T, Hk, D) or slot_mapping.shape != (T,):
+        raise ValueError("k, v must be [T, Hk, D] and slot_mapping [T]")
+    if dtype_code(k) != dtype_code(pool.dtype):
+        raise ValueError("rows must have the pool's dtype")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError("k/v rows must be contiguous within a token")
+    _check(lib().pkv_reshape_and_cache(_ptr(k), _ptr(v), _ptr(slot_mapping), T, k.stride(0), v.stride(0),
+                                       pool.k_base, pool.v_base, pool.num_blocks, Hk, D, pool.block_size,
+                                       dtype_code(pool.dtype), _stream(stream)), "pkv_reshape_and_cache")
+
+
+def paged_attention_decode_flat(out, q, pool: SpanPool, span_ids, seq_lens, scale: float, max_seq_len: int,
+                                partition_size: int = 512, workspace=None, stream=None) -> None:
+    """Decode attention over flat spans (no block table): row s reads span span_ids[s]."""
+    import torch
+    S, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != (S, Hq, D) or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [S, Hq, D] with the pool's head_dim")
+    if span_ids.dtype != torch.int32 or span_ids.shape != (S,):
+        raise ValueError("span_ids must be int32 [S]")
+    need = workspace_size(S, Hq, D, max_seq_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_paged_attention_decode_flat(
+        _ptr(out), dtype_code(out), _ptr(q), pool.k_base, pool.v_base, _ptr(span_ids), pool.blocks_per_span,
+        _ptr(seq_lens), S, Hq, pool.n_kv_heads, D, pool.block_size, pool.num_blocks, float(scale),
+        int(max_seq_len), int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        dtype_code(q), 0, _stream(stream)), "pkv_paged_attention_decode_flat")
 
 
 def timing_enable(on: bool = True) -> None:

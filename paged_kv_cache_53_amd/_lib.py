@@ -19,6 +19,12 @@ class pkv_stats(C.Structure):
                 ("num_seqs", C.c_int64), ("live_tokens", C.c_int64), ("allocated_slots", C.c_int64)]
 
 
+class pkv_span_info(C.Structure):
+    _fields_ = [("k_base", C.c_void_p), ("v_base", C.c_void_p), ("blocks_per_span", C.c_int32),
+                ("num_blocks", C.c_int32), ("chunk_bytes", C.c_size_t), ("span_bytes", C.c_size_t),
+                ("mapped_bytes", C.c_size_t), ("spare_bytes", C.c_size_t)]
+
+
 class pkv_kernel_time(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("launches", C.c_int32), ("total_ms", C.c_double)]
 
@@ -45,6 +51,15 @@ SIGNATURES = {
     "pkv_paged_attention_decode_fp8": (C.c_int, [P, C.c_int, P, C.c_int, P, P, C.c_float, C.c_float, P, I32, P,
                                                  I32, I32, I32, I32, I32, I32, C.c_float, I32, I32, P, SZ,
                                                  C.c_uint32, P]),
+    "pkv_paged_attention_decode_flat": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                                  C.c_float, I32, I32, P, SZ, C.c_int, C.c_uint32, P]),
+    "pkv_span_pool_create": (C.c_int, [I32, I32, I32, I32, I32, C.c_int, SZ, C.POINTER(P)]),
+    "pkv_span_pool_destroy": (None, [P]),
+    "pkv_span_reserve": (C.c_int, [P, I32, I32]),
+    "pkv_span_release": (C.c_int, [P, I32]),
+    "pkv_span_pool_trim": (C.c_int, [P]),
+    "pkv_span_pool_info": (C.c_int, [P, C.POINTER(pkv_span_info)]),
+    "pkv_span_mapped_tokens": (I32, [P, I32]),
     "pkv_allocator_create": (C.c_int, [I32, I32, PI32, C.POINTER(P)]),
     "pkv_allocator_destroy": (None, [P]),
     "pkv_alloc": (C.c_int, [P, I64, I32, PI64, PI32, PI32]),

@@ -72,13 +72,14 @@ Timing& timing() {
 std::mutex cap_mu;
 std::unordered_map<int64_t, int32_t> cap_cache;
 
-hipError_t grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size, int32_t* cap) {
+hipError_t grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group, int block_size,
+                    int32_t* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4),
-  // the MFMA path one per storage type
-  const int variant = path == 1 ? (kv_fp8 ? 4 : 3) : (group == 1 ? 0 : group == 2 ? 1 : 2);
+  // the MFMA path one per storage type and one for flat spans
+  const int variant = path == 1 ? (flat ? 5 : kv_fp8 ? 4 : 3) : (group == 1 ? 0 : group == 2 ? 1 : 2);
   const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 8 + variant) * 64) +
                       block_size;
   {
@@ -89,7 +90,7 @@ hipError_t grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, i
       return hipSuccess;
     }
   }
-  e = decode_main_grid_cap(dtype, kv_fp8, head_dim, path, group, block_size, cap);
+  e = decode_main_grid_cap(dtype, kv_fp8, flat, head_dim, path, group, block_size, cap);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> g(cap_mu);
   cap_cache[key] = *cap;
@@ -285,15 +286,17 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
 
 namespace {
 
-// Both decode entry points.  q_dtype: the type of q (and of out unless out is fp32); kv_fp8: the
-// pools hold E4M3 codes with scales k_scale / v_scale (else they hold q_dtype).
+// Every decode entry point.  q_dtype: the type of q (and of out unless out is fp32); kv_fp8: the
+// pools hold E4M3 codes with scales k_scale / v_scale (else they hold q_dtype); flat_bps > 0: flat
+// spans of flat_bps blocks, block_tables then holds one span index per row.
 int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
                 bool kv_fp8, float k_scale, float v_scale, const int32_t* block_tables,
                 int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                 int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                uint32_t flags, void* stream) {
+                uint32_t flags, void* stream, int32_t flat_bps = 0) {
   const int kv_dtype = q_dtype;   // the compute type of the kernels
+  const bool flat = flat_bps > 0;
   if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV)) return PKV_ERR_INVALID;
   // ---- shape and type checks
   if (!valid_dtype(kv_dtype) || !(out_dtype == kv_dtype || out_dtype == PKV_F32)) return PKV_ERR_INVALID;
@@ -315,7 +318,13 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
     path = 1;   // MFMA for every group size (padded heads): measured 2 % faster than the vector path at G = 1
   }
   const int64_t max_blocks = (static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size;
-  if (block_table_stride < max_blocks || block_table_stride < 0) return PKV_ERR_INVALID;
+  if (flat) {
+    if (kv_fp8 || kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;   // flat spans: 16-bit KV
+    if (max_blocks > flat_bps || num_blocks % flat_bps) return PKV_ERR_INVALID;
+    if (flags & PKV_DECODE_SHARED_KV) return PKV_ERR_UNSUPPORTED;    // spans are never shared
+  } else if (block_table_stride < max_blocks || block_table_stride < 0) {
+    return PKV_ERR_INVALID;
+  }
   const int32_t P = partition_tokens(max_seq_len, partition_size);
   const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
   const int64_t unit_bound = static_cast<int64_t>(num_seqs) * max_parts * n_kv_heads;
@@ -356,9 +365,10 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
   a.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
   a.scale_log2 = (kv_fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
   a.v_scale = kv_fp8 ? v_scale : 1.f;
+  a.flat_bps = flat ? flat_bps : 0;
 
   int32_t cap = 0;
-  if (grid_cap(kv_dtype, kv_fp8, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
+  if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
   const int32_t grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -393,6 +403,18 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
   return decode_impl(out, out_dtype, q, kv_dtype, k_pool, v_pool, false, 1.f, 1.f, block_tables,
                      block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size,
                      num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags, stream);
+}
+
+int pkv_paged_attention_decode_flat(void* out, int out_dtype, const void* q, const void* k_base, const void* v_base,
+                                    const int32_t* span_ids, int32_t blocks_per_span, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, float scale, int32_t max_seq_len,
+                                    int32_t partition_size, void* workspace, size_t workspace_bytes, int kv_dtype,
+                                    uint32_t flags, void* stream) {
+  if (blocks_per_span <= 0) return PKV_ERR_INVALID;
+  return decode_impl(out, out_dtype, q, kv_dtype, k_base, v_base, false, 1.f, 1.f, span_ids, 1, seq_lens,
+                     num_seqs, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks, scale, max_seq_len,
+                     partition_size, workspace, workspace_bytes, flags, stream, blocks_per_span);
 }
 
 int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool,

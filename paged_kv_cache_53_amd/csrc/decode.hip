@@ -288,7 +288,9 @@ struct Unit {
   const T* vbase;
 };
 
-template <typename T>
+// FLAT: the row's blocks are the consecutive blocks of its span (block_tables holds one span index
+// per row): the first block id is computed, not read from a table.
+template <typename T, bool FLAT>
 __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) {
   Unit<T> u;
   const int pair = id / a.n_kv_heads;
@@ -299,8 +301,13 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   const int tok0 = u.part * a.part_tokens;
   u.ntok = min(a.part_tokens, L - tok0);
   u.nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  u.bt = a.block_tables + static_cast<int64_t>(u.s) * a.bt_stride + (tok0 >> a.log2_block);
-  u.id_first = ld_uniform(u.bt, 0);
+  if constexpr (FLAT) {
+    u.bt = a.block_tables;   // unused
+    u.id_first = ld_uniform(a.block_tables, u.s) * a.flat_bps + (tok0 >> a.log2_block);
+  } else {
+    u.bt = a.block_tables + static_cast<int64_t>(u.s) * a.bt_stride + (tok0 >> a.log2_block);
+    u.id_first = ld_uniform(u.bt, 0);
+  }
   u.kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(u.kvh) * chunk;
   u.vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(u.kvh) * chunk;
   return u;
@@ -322,23 +329,21 @@ struct Tile16 {
   // ntok tokens, pools offset to its KV head), completion explicitly waited when E (vload).
   // Block ids are wave-uniform scalar loads (the first one was read when the unit was opened);
   // table entries past the unit's last block are never read (those tokens reuse the first id
-  // and are masked in the compute).
-  template <int Bsz, bool E, bool NT>
+  // and are masked in the compute).  FLAT: block i of the unit is id_first + i, no table.
+  template <int Bsz, bool E, bool NT, bool FLAT>
   __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const T* kbase,
                         const T* vbase, int t0, int64_t blk_stride) {
     constexpr int X = Kv<T>::X;
     constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     const int first = t0 / Bsz;
-    int id0 = first == 0 ? id_first : ld_uniform(bt, first);
-    id0 = min(max(id0, 0), a.num_blocks - 1);
+    int id0 = FLAT ? id_first + first : (first == 0 ? id_first : ld_uniform(bt, first));
     int id1 = id0;
     if constexpr (NB == 2) {
-      if (t0 + 8 < ntok) {
-        id1 = ld_uniform(bt, first + 1);
-        id1 = min(max(id1, 0), a.num_blocks - 1);
-      }
+      if (t0 + 8 < ntok) id1 = FLAT ? id_first + first + 1 : ld_uniform(bt, first + 1);
     }
+    id0 = min(max(id0, 0), a.num_blocks - 1);
+    id1 = min(max(id1, 0), a.num_blocks - 1);
     const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
     const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
 #pragma unroll
@@ -377,7 +382,7 @@ struct Tile32F8 {
   u32x4 kf[2][NK];
   u32x2 vf[D / 16];
 
-  template <int Bsz, bool E, bool NT>
+  template <int Bsz, bool E, bool NT, bool FLAT>
   __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const E4M3* kbase,
                         const E4M3* vbase, int t0, int64_t blk_stride) {
     constexpr int NB = 32 / Bsz;                 // blocks per tile: 4, 2 or 1
@@ -385,11 +390,12 @@ struct Tile32F8 {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     const int first = t0 / Bsz;
     int id[NB];
-    id[0] = first == 0 ? id_first : ld_uniform(bt, first);
+    id[0] = FLAT ? id_first + first : (first == 0 ? id_first : ld_uniform(bt, first));
 #pragma unroll
     for (int j = 1; j < NB; ++j) {
       id[j] = id[0];
-      if (t0 + j * Bsz < ntok) id[j] = ld_uniform(bt, first + j);   // later blocks of the tile, if any token is real
+      if (t0 + j * Bsz < ntok)   // later blocks of the tile, if any token is real
+        id[j] = FLAT ? id_first + first + j : ld_uniform(bt, first + j);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) id[j] = min(max(id[j], 0), a.num_blocks - 1);
@@ -828,7 +834,7 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
 // issues the same loads on every path.  The next unit is claimed a few tiles before it is
 // needed.
 // KV: the storage type of the pools (the tile's element); Math carries the compute type.
-template <typename KV, int D, int Bsz, class Math, bool NT>
+template <typename KV, int D, int Bsz, class Math, bool NT, bool FLAT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
   using Tile = typename Math::Tile;
@@ -848,7 +854,7 @@ void decode_kernel(DecodeArgs a) {
   tie<E>(pending);
   const int first = __builtin_amdgcn_readfirstlane(pending);
   if (first >= total) return;
-  Unit<KV> uc = open_unit<KV>(a, first, chunk);   // compute cursor
+  Unit<KV> uc = open_unit<KV, FLAT>(a, first, chunk);   // compute cursor
   Unit<KV> ui = uc;                              // issue cursor
   Unit<KV> un_next = uc;                         // the claimed unit after the issue cursor's
   u32x4 qr[Math::QH][NQ];
@@ -884,7 +890,7 @@ void decode_kernel(DecodeArgs a) {
     // reads, done here a few tiles before the switch instead of on its path).
     auto open_next = [&](int un) __attribute__((always_inline)) {
       if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
-        un_next = open_unit<KV>(a, un, chunk);
+        un_next = open_unit<KV, FLAT>(a, un, chunk);
         fl |= kNext;
       } else {
         fl |= kEnded;
@@ -926,7 +932,7 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    Y.template issue<Bsz, E, NT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+    Y.template issue<Bsz, E, NT, FLAT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
                                  is_real ? +ui.ntok : +uc.ntok,
                                  is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
                                  is_real ? +ti : tc_now, blk_stride);
@@ -1057,19 +1063,25 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename KV, int D, class Math, bool NT>
+template <typename KV, int D, class Math, bool NT, bool FLAT = false>
 const void* kernel_ptr_b(int block_size) {
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT>);
-    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT>);
-    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT, FLAT>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT, FLAT>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT, FLAT>);
     default: return nullptr;
   }
 }
 
-// T: the type of q and of the outputs; fp8: the pools hold E4M3 codes (MFMA path only)
+// T: the type of q and of the outputs; fp8: the pools hold E4M3 codes (MFMA path only); flat: rows
+// read consecutive blocks of their span (16-bit KV on MFMA, streamed loads only)
 template <typename T, int D>
-const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8) {
+const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8, bool flat) {
+  if (flat) {
+    if constexpr (sizeof(T) == 2)
+      if (path == 1 && !fp8 && nt) return kernel_ptr_b<T, D, MfmaMath<T, D>, true, true>(block_size);
+    return nullptr;
+  }
   if (path == 1) {
     if constexpr (sizeof(T) == 2) {
       if (fp8)
@@ -1091,9 +1103,9 @@ const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8)
 }
 
 template <typename T>
-const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt, bool fp8) {
-  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt, fp8)
-                         : kernel_ptr_d<T, 64>(path, group, block_size, nt, fp8);
+const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt, bool fp8, bool flat) {
+  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt, fp8, flat)
+                         : kernel_ptr_d<T, 64>(path, group, block_size, nt, fp8, flat);
 }
 
 }  // namespace
@@ -1107,10 +1119,11 @@ hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipS
 
 hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, bool nt,
                               int32_t grid, hipStream_t st) {
+  const bool flat = a.flat_bps > 0;
   const void* fn =
-      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt, kv_fp8)
-      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt, kv_fp8)
-                         : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt, kv_fp8);
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat)
+                         : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(64), args, 0, st);
@@ -1131,12 +1144,13 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
   return hipGetLastError();
 }
 
-hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size,
-                                int32_t* cap) {
+hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
+                                int block_size, int32_t* cap) {
   // both cache policies compile to the same code shape: the streamed variant stands for both
-  const void* fn = dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true, kv_fp8)
-                   : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true, kv_fp8)
-                                      : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true, kv_fp8);
+  const void* fn =
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true, kv_fp8, flat)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true, kv_fp8, flat)
+                         : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true, kv_fp8, flat);
   if (!fn) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -54,6 +54,7 @@ struct DecodeArgs {
   float scale_log2;      // scale * log2(e) (times the key scale of a quantised cache): scores
                          // are kept in the base-2 domain
   float v_scale;         // value scale of a quantised cache (1 otherwise)
+  int32_t flat_bps;      // > 0: flat spans of this many blocks, block_tables holds one span per row
 };
 
 // Workspace carve-up shared by the size query and the launcher.
@@ -83,8 +84,11 @@ hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int h
                               int32_t grid, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.
-hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, int head_dim, int path, int group, int block_size,
-                                int32_t* cap);
+hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
+                                int block_size, int32_t* cap);
+
+// Physical memory of a flat-span pool is mapped in chunks of this size unless the caller picks another.
+constexpr size_t PKV_SPAN_DEFAULT_CHUNK = size_t{2} << 20;
 
 // ---------------------------------------------------------------- timing hooks
 void timing_before(int kernel, hipStream_t stream);

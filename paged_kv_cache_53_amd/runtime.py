@@ -14,6 +14,11 @@ DecodeBatch    a fixed set of sequences decoded together: device block tables an
                  5. paged decode (plan, main, merge kernels)
                Host work for step i+1 overlaps the GPU work of step i; the host waits only
                before reusing a staging buffer that a copy may still be reading.
+FlatKVCache    the flat-span alternative: one contiguous virtual span per sequence (SpanPool),
+               physical memory mapped as the sequence grows, no block table.
+FlatDecodeBatch  one decode step over flat spans: span backing grown on the host when a token
+               starts an unmapped chunk, slots staged as above, the append kernel bumps the
+               lengths, scatter, then decode that computes block ids from each row's span.
 """
 from __future__ import annotations
 
@@ -23,8 +28,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (Allocator, append_slots, copy_blocks, key_pool_shape, paged_attention_decode,
-               reshape_and_cache, value_pool_shape, workspace_size)
+from . import (Allocator, SpanPool, append_slots, copy_blocks, key_pool_shape, paged_attention_decode,
+               paged_attention_decode_flat, reshape_and_cache, reshape_and_cache_spans, value_pool_shape,
+               workspace_size)
 
 
 class PagedKVCache:
@@ -142,3 +148,113 @@ class DecodeBatch:
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
                                shared_kv=c.has_shared_blocks(), **c.scales)
+
+
+class FlatKVCache:
+    """Sequences in flat spans of a SpanPool: a sequence takes a free span when it first appends and
+    gives it back (unmapped) when freed."""
+
+    def __init__(self, max_seqs: int, max_tokens: int, block_size: int, n_kv_heads: int, head_dim: int, dtype,
+                 device="cuda", chunk_bytes: int = 0):
+        self.pool = SpanPool(max_seqs, max_tokens, n_kv_heads, head_dim, block_size, dtype, chunk_bytes)
+        self.block_size, self.n_kv_heads, self.head_dim, self.dtype = block_size, n_kv_heads, head_dim, dtype
+        self.device = device
+        self.free_spans = list(range(max_seqs))
+        self.span_of, self.lens = {}, {}
+        self.mapped = [0] * max_seqs      # tokens backed per span, mirrored on the host
+
+    def span(self, seq: int) -> int:
+        if seq not in self.span_of:
+            if not self.free_spans:
+                raise MemoryError("no free span")
+            self.span_of[seq] = self.free_spans.pop(0)
+            self.lens[seq] = 0
+        return self.span_of[seq]
+
+    def ensure(self, span: int, n_tokens: int) -> None:
+        """Backs tokens [0, n_tokens) of a span; a host call only when a new chunk is needed."""
+        if n_tokens > self.mapped[span]:
+            self.pool.reserve(span, n_tokens)
+            self.mapped[span] = self.pool.mapped_tokens(span)
+
+    def slots(self, seq: int, n: int):
+        sp = self.span(seq)
+        L = self.lens[seq]
+        self.ensure(sp, L + n)
+        return [self.pool.slot(sp, L + i) for i in range(n)]
+
+    def append(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        n = int(k.shape[0])
+        sl = self.slots(seq, n)
+        self.lens[seq] += n
+        if n:
+            reshape_and_cache_spans(k, v, torch.tensor(sl, dtype=torch.int64, device=self.device), self.pool)
+
+    def free(self, seq: int) -> None:
+        sp = self.span_of.pop(seq)
+        del self.lens[seq]
+        torch.cuda.current_stream().synchronize()   # nothing on the device may still touch the span
+        self.pool.release(sp)
+        self.mapped[sp] = 0
+        self.free_spans.append(sp)
+
+
+class FlatDecodeBatch:
+    def __init__(self, cache: FlatKVCache, seq_ids: Sequence[int], n_q_heads: int, max_seq_len: int,
+                 partition_size: int = 512, scale: Optional[float] = None):
+        self.cache = cache
+        self.seq_ids = [int(x) for x in seq_ids]
+        self.S = len(self.seq_ids)
+        self.n_q_heads, self.max_seq_len, self.partition_size = n_q_heads, max_seq_len, partition_size
+        self.scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else scale
+        spans = [cache.span(s) for s in self.seq_ids]
+        lens = np.array([cache.lens[s] for s in self.seq_ids], dtype=np.int32)
+        if int(lens.max(initial=0)) > max_seq_len:
+            raise ValueError("a sequence is already longer than max_seq_len")
+        dev = cache.device
+        self.spans = np.array(spans, dtype=np.int64)
+        self.span_ids = torch.tensor(spans, dtype=torch.int32, device=dev)
+        self.seq_lens = torch.from_numpy(lens).to(dev)
+        self.host_lens = lens.astype(np.int64)
+        # the append kernel bumps the lengths; the table it also writes is scratch (flat spans have none),
+        # wide enough that no row's position falls outside it (the kernel skips such rows entirely)
+        self.scratch_table = torch.zeros((self.S, max(1, -(-max_seq_len // cache.block_size))), dtype=torch.int32,
+                                         device=dev)
+        self.workspace = torch.empty(max(256, workspace_size(self.S, n_q_heads, cache.head_dim, max_seq_len,
+                                                               partition_size)), dtype=torch.uint8, device=dev)
+        self.slot_stage = [torch.empty(self.S, dtype=torch.int64, pin_memory=True) for _ in range(2)]
+        self.slot_stage_np = [t.numpy() for t in self.slot_stage]
+        self.stage_done = [None, None]
+        self.slot_dev = torch.empty(self.S, dtype=torch.int64, device=dev)
+        self.steps = 0
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor) -> None:
+        """One decode step for every row: back the new token, write its K/V, attend over all tokens."""
+        c = self.cache
+        if int(self.host_lens.max(initial=0)) + 1 > self.max_seq_len:
+            raise ValueError("decode step would exceed max_seq_len")
+        i = self.steps & 1
+        if self.stage_done[i] is not None:
+            self.stage_done[i].synchronize()
+        pos = self.host_lens
+        for r in np.nonzero(pos + 1 > np.asarray(c.mapped)[self.spans])[0].tolist():
+            c.ensure(int(self.spans[r]), int(pos[r]) + 1)     # a token that starts an unmapped chunk
+        B, bps = c.block_size, c.pool.blocks_per_span
+        self.slot_stage_np[i][:] = (self.spans * bps + pos // B) * B + pos % B
+        self.host_lens += 1
+        for r, s in enumerate(self.seq_ids):
+            c.lens[s] = int(self.host_lens[r])
+        self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.stage_done[i] = ev
+        append_slots(self.slot_dev, self.scratch_table, self.seq_lens, B)
+        reshape_and_cache_spans(k_new, v_new, self.slot_dev, c.pool)
+        paged_attention_decode_flat(out, q, c.pool, self.span_ids, self.seq_lens, self.scale, self.max_seq_len,
+                                    self.partition_size, workspace=self.workspace)
+        self.steps += 1
+
+    def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
+        c = self.cache
+        paged_attention_decode_flat(out, q, c.pool, self.span_ids, self.seq_lens, self.scale, self.max_seq_len,
+                                    self.partition_size, workspace=self.workspace)

@@ -170,6 +170,41 @@ def test_fp8_entries_reject_bad_arguments_before_launch():
     assert lib.pkv_copy_blocks(16, 16, 16, 1, 10, 1, 8, 1, FP8, None) == pkv.PKV_ERR_UNSUPPORTED   # 8-byte blocks
 
 
+def test_flat_entries_reject_bad_arguments_before_any_hip_call():
+    lib = pkv.lib()
+    import ctypes as C
+    h = C.c_void_p()
+    BF16 = pkv.PKV_BF16
+    c = lib.pkv_span_pool_create
+    assert c(0, 100, 2, 128, 16, BF16, 0, C.byref(h)) == pkv.PKV_ERR_INVALID        # no spans
+    assert c(4, 0, 2, 128, 16, BF16, 0, C.byref(h)) == pkv.PKV_ERR_INVALID          # no tokens
+    assert c(4, 100, 2, 100, 16, BF16, 0, C.byref(h)) == pkv.PKV_ERR_INVALID        # head_dim % 8
+    assert c(4, 100, 2, 128, 16, 9, 0, C.byref(h)) == pkv.PKV_ERR_INVALID           # no such type
+    assert c(4, 100, 2, 128, 16, BF16, 0, None) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_span_reserve(None, 0, 10) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_span_release(None, 0) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_span_pool_trim(None) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_span_mapped_tokens(None, 0) == -1
+    lib.pkv_span_pool_destroy(None)
+    d = lib.pkv_paged_attention_decode_flat
+
+    def dec(**kw):
+        a = dict(out=16, odt=BF16, q=16, k=16, v=16, spans=16, bps=64, lens=16, S=2, Hq=8, Hk=2, D=128, B=16,
+                 N=256, scale=0.1, maxL=1024, P=512, ws=256, wsb=1 << 30, dt=BF16, flags=0)
+        a.update(kw)
+        return d(a["out"], a["odt"], a["q"], a["k"], a["v"], a["spans"], a["bps"], a["lens"], a["S"], a["Hq"],
+                 a["Hk"], a["D"], a["B"], a["N"], a["scale"], a["maxL"], a["P"], a["ws"], a["wsb"], a["dt"],
+                 a["flags"], None)
+
+    assert dec(S=0) == pkv.PKV_OK
+    assert dec(bps=0) == pkv.PKV_ERR_INVALID
+    assert dec(maxL=1025) == pkv.PKV_ERR_INVALID                   # 65 blocks do not fit a 64-block span
+    assert dec(N=250) == pkv.PKV_ERR_INVALID                       # not a whole number of spans
+    assert dec(dt=pkv.PKV_F32, odt=pkv.PKV_F32) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(flags=pkv.PKV_DECODE_SHARED_KV) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(spans=None) == pkv.PKV_ERR_INVALID
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
