@@ -160,16 +160,21 @@ class FlatKVCache:
         self.block_size, self.n_kv_heads, self.head_dim, self.dtype = block_size, n_kv_heads, head_dim, dtype
         self.device = device
         self.free_spans = list(range(max_seqs))
-        self.span_of, self.lens = {}, {}
-        self.mapped = [0] * max_seqs      # tokens backed per span, mirrored on the host
+        self.span_of = {}
+        self.span_len = np.zeros(max_seqs, dtype=np.int64)   # tokens held per span
+        self.mapped = np.zeros(max_seqs, dtype=np.int64)     # tokens backed per span, mirrored on the host
 
     def span(self, seq: int) -> int:
         if seq not in self.span_of:
             if not self.free_spans:
                 raise MemoryError("no free span")
-            self.span_of[seq] = self.free_spans.pop(0)
-            self.lens[seq] = 0
+            sp = self.free_spans.pop(0)
+            self.span_of[seq] = sp
+            self.span_len[sp] = 0
         return self.span_of[seq]
+
+    def length(self, seq: int) -> int:
+        return int(self.span_len[self.span_of[seq]])
 
     def ensure(self, span: int, n_tokens: int) -> None:
         """Backs tokens [0, n_tokens) of a span; a host call only when a new chunk is needed."""
@@ -179,20 +184,20 @@ class FlatKVCache:
 
     def slots(self, seq: int, n: int):
         sp = self.span(seq)
-        L = self.lens[seq]
+        L = int(self.span_len[sp])
         self.ensure(sp, L + n)
         return [self.pool.slot(sp, L + i) for i in range(n)]
 
     def append(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
         n = int(k.shape[0])
         sl = self.slots(seq, n)
-        self.lens[seq] += n
+        self.span_len[self.span_of[seq]] += n
         if n:
             reshape_and_cache_spans(k, v, torch.tensor(sl, dtype=torch.int64, device=self.device), self.pool)
 
     def free(self, seq: int) -> None:
         sp = self.span_of.pop(seq)
-        del self.lens[seq]
+        self.span_len[sp] = 0
         torch.cuda.current_stream().synchronize()   # nothing on the device may still touch the span
         self.pool.release(sp)
         self.mapped[sp] = 0
@@ -208,7 +213,7 @@ class FlatDecodeBatch:
         self.n_q_heads, self.max_seq_len, self.partition_size = n_q_heads, max_seq_len, partition_size
         self.scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else scale
         spans = [cache.span(s) for s in self.seq_ids]
-        lens = np.array([cache.lens[s] for s in self.seq_ids], dtype=np.int32)
+        lens = cache.span_len[spans].astype(np.int32)
         if int(lens.max(initial=0)) > max_seq_len:
             raise ValueError("a sequence is already longer than max_seq_len")
         dev = cache.device
@@ -237,13 +242,12 @@ class FlatDecodeBatch:
         if self.stage_done[i] is not None:
             self.stage_done[i].synchronize()
         pos = self.host_lens
-        for r in np.nonzero(pos + 1 > np.asarray(c.mapped)[self.spans])[0].tolist():
+        for r in np.nonzero(pos + 1 > c.mapped[self.spans])[0].tolist():
             c.ensure(int(self.spans[r]), int(pos[r]) + 1)     # a token that starts an unmapped chunk
         B, bps = c.block_size, c.pool.blocks_per_span
         self.slot_stage_np[i][:] = (self.spans * bps + pos // B) * B + pos % B
         self.host_lens += 1
-        for r, s in enumerate(self.seq_ids):
-            c.lens[s] = int(self.host_lens[r])
+        c.span_len[self.spans] = self.host_lens
         self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
