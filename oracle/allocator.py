@@ -34,6 +34,23 @@ result, so the C++ allocator can be compared bit for bit):
   already taken some blocks);
 * only a write into the partly filled last block can hit a shared block, so
   copy-on-write is checked on the first token an ``alloc`` appends.
+
+Swapping to host memory: instead of evicting a sequence and recomputing its cache, an engine
+can move its blocks to host memory and bring them back later ("Reserve for the worst case, or
+page", section "What this model leaves out").  The pages give no policy; the readings are:
+
+* host memory is a fixed number of host slots of one block each, handed out from the head of
+  their own free list and returned to its tail (the device pool's discipline);
+* ``swap_out(seq)`` moves every block of a device-resident sequence, in logical order: each takes
+  the next host slot, gives a (device block, host slot) copy pair, and loses the sequence's
+  reference exactly as ``free_seq`` drops it (a block still shared stays on the device for its
+  other sequences; the host copy is this sequence's own);
+* ``swap_in(seq)`` takes fresh device blocks in logical order, gives (host slot, device block)
+  pairs and returns the host slots, in order, to the tail of their list; the sequence comes
+  back with private blocks and its length;
+* both are all or nothing (too few host slots, or too few device blocks, change nothing); a
+  swapped-out sequence cannot append or be forked until it is back, and freeing it returns its
+  host slots.
 """
 from __future__ import annotations
 
@@ -58,6 +75,9 @@ class BlockAllocatorModel:
         self.ref: List[int] = [0] * num_blocks  # sequences whose table holds the block
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.host_free: List[int] = []                          # head = next host slot handed out
+        self.num_host = 0
+        self.swapped: Dict[int, Tuple[List[int], int]] = {}    # seq -> (host slots, length)
 
     # -- queries -------------------------------------------------------------
     def block_table(self, seq: int) -> List[int]:
@@ -87,6 +107,8 @@ class BlockAllocatorModel:
         """Append n tokens to seq (created empty if unknown); returns (slots, copy pairs)."""
         if n < 0:
             raise ValueError("n must be >= 0")
+        if seq in self.swapped:
+            raise ValueError(f"sequence {seq} is swapped out")
         B = self.B
         table = self.tables.get(seq, [])
         L = self.lens.get(seq, 0)
@@ -118,7 +140,7 @@ class BlockAllocatorModel:
         """Child shares the parent's first ceil(n/B) blocks (n = -1: the parent's whole length)."""
         if parent not in self.tables:
             raise KeyError(parent)
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             raise ValueError(f"sequence {child} already exists")
         plen = self.lens[parent]
         if n < 0:
@@ -134,13 +156,57 @@ class BlockAllocatorModel:
 
     def free_seq(self, seq: int) -> None:
         """Drop seq: each of its blocks loses one reference, in logical order; at zero it rejoins
-        the tail of the free list."""
+        the tail of the free list.  A swapped-out sequence returns its host slots instead."""
+        if seq in self.swapped:
+            slots, _ = self.swapped.pop(seq)
+            self.host_free.extend(slots)
+            return
         table = self.tables.pop(seq)
         del self.lens[seq]
         for b in table:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
+
+    # -- swapping to host memory ------------------------------------------------
+    def set_swap_space(self, num_host: int) -> None:
+        """num_host host slots, handed out in order 0, 1, ..."""
+        if num_host < 0 or self.num_host:
+            raise ValueError("swap space is set once, with a non-negative size")
+        self.num_host = num_host
+        self.host_free = list(range(num_host))
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """Move a device-resident sequence to host slots; returns (device block, host slot) pairs."""
+        table = self.tables[seq]
+        if len(table) > len(self.host_free):
+            raise OutOfBlocks(f"need {len(table)} host slots, {len(self.host_free)} free")
+        pairs = []
+        for b in table:
+            h = self.host_free.pop(0)
+            pairs.append((b, h))
+        L = self.lens[seq]
+        self.free_seq(seq)
+        self.swapped[seq] = ([h for _, h in pairs], L)
+        return pairs
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """Bring a swapped-out sequence back into fresh device blocks; returns (host slot, device
+        block) pairs."""
+        slots, L = self.swapped[seq]
+        if len(slots) > len(self.free):
+            raise OutOfBlocks(f"need {len(slots)} blocks, {len(self.free)} free")
+        del self.swapped[seq]
+        table, pairs = [], []
+        for h in slots:
+            b = self.free.pop(0)
+            self.ref[b] = 1
+            table.append(b)
+            pairs.append((h, b))
+        self.host_free.extend(slots)
+        self.tables[seq] = table
+        self.lens[seq] = L
+        return pairs
 
     # -- convenience -----------------------------------------------------------
     def run(self, ops) -> None:

@@ -119,3 +119,18 @@ def flat_span_table(span: int, blocks_per_span: int, L: int, B: int):
     if nb > blocks_per_span:
         raise ValueError("sequence longer than its span")
     return [span * blocks_per_span + i for i in range(nb)]
+
+
+def move_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray, pairs) -> None:
+    """Block copies between two block arrays of the pools' layout (a device pool and host swap
+    space): for each (src, dst) pair, block dst of dst_k / dst_v becomes a bit copy of block src
+    of src_k / src_v ("Reserve for the worst case, or page", section "What this model leaves out":
+    a preempted sequence's blocks go to host memory and come back).  Pairs with an id outside
+    either array are skipped."""
+    ns, nd = src_k.shape[0], dst_k.shape[0]
+    for s, d in pairs:
+        s, d = int(s), int(d)
+        if not (0 <= s < ns and 0 <= d < nd):
+            continue
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
