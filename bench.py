@@ -69,6 +69,8 @@ def parse():
                    help="run only a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     p.add_argument("--copy-blocks", action="store_true",
                    help="time the copy-on-write block copy kernel alone (4096 random block pairs)")
+    p.add_argument("--swap", action="store_true",
+                   help="time block moves between the pool and pinned host swap space (4096 blocks each way)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                         "--copy-calibration into the traffic record (CPU only; writes --pmc-out)")
@@ -422,6 +424,8 @@ def main():
 
     if args.copy_blocks:
         return bench_copy_blocks(args)
+    if args.swap:
+        return bench_swap(args)
 
     w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
@@ -503,6 +507,69 @@ def bench_copy_blocks(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
                      "bytes_per_launch": moved, "avg_launch_us": round(us, 2)}}), flush=True)
+
+
+def bench_swap(args):
+    """Swap traffic on the workload's pool shape: 4096 random blocks from an 8192-block device pool to
+    pinned host slots and back per call.  Bytes = blocks x block bytes x 2 pools, each way.  Beside
+    it, a plain pinned-to-device copy of the same bytes (one contiguous buffer) gives the host link's
+    practical rate."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_53_amd as pkv
+    import workloads as wl
+    w = wl.build(args.config, block_size=args.block_size)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    n, N, H = 4096, 8192, 4096
+    kp = torch.empty(pkv.key_pool_shape(N, w.n_kv_heads, w.head_dim, w.block_size, dt), dtype=dt, device="cuda")
+    vp = torch.empty(pkv.value_pool_shape(N, w.n_kv_heads, w.head_dim, w.block_size), dtype=dt, device="cuda")
+    kh = torch.empty(pkv.key_pool_shape(H, w.n_kv_heads, w.head_dim, w.block_size, dt), dtype=dt, pin_memory=True)
+    vh = torch.empty(pkv.value_pool_shape(H, w.n_kv_heads, w.head_dim, w.block_size), dtype=dt, pin_memory=True)
+    rng = np.random.default_rng([w.seed, 8])
+    dev, host = rng.permutation(N)[:n], rng.permutation(H)[:n]
+    out_pairs = torch.from_numpy(np.stack([dev, host], 1).astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([host, rng.permutation(N)[:n]], 1).astype(np.int32)).cuda()
+    block_bytes = w.n_kv_heads * w.head_dim * w.block_size * w.esize
+    moved = n * block_bytes * 2
+    res = {}
+    for name, fn in (("to_host", lambda: pkv.swap_blocks(out_pairs, kp, vp, kh, vh)),
+                     ("to_device", lambda: pkv.swap_blocks(in_pairs, kh, vh, kp, vp))):
+        for _ in range(args.warmup):
+            fn()
+        pkv.timing_select(["swap_blocks"])
+        pkv.timing_enable(True)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        k, ms = pkv.timing_collect()["swap_blocks"]
+        pkv.timing_enable(False)
+        pkv.timing_select(None)
+        us = ms / k * 1e3
+        res[name] = {"avg_us": round(us, 1), "GBps": round(moved / (us * 1e-6) / 1e9, 2)}
+    flat_h = torch.empty(moved // 2, dtype=torch.uint8, pin_memory=True)
+    flat_d = torch.empty(moved // 2, dtype=torch.uint8, device="cuda")
+    plain = {}
+    for name, (dst, src) in (("to_host", (flat_h, flat_d)), ("to_device", (flat_d, flat_h))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        plain[name] = {"avg_us": round(us, 1), "GBps": round(moved / 2 / (us * 1e-6) / 1e9, 2)}
+    print(json.dumps({
+        "metric": "swap block moves between the pool and pinned host memory, GB/s each way",
+        "value": res["to_host"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} pool shape, {n} blocks per call, 8192-block pool, {H} host slots",
+                   "block_bytes_per_pool": block_bytes, "bytes_per_call": moved},
+        "swap_kernel": res, "plain_contiguous_copy_same_bytes": plain}), flush=True)
 
 
 def sweep(args):

@@ -64,7 +64,8 @@ enum {
   PKV_K_DECODE = 3,
   PKV_K_DECODE_REDUCE = 4,
   PKV_K_COPY_BLOCKS = 5,
-  PKV_K_COUNT = 6
+  PKV_K_SWAP_BLOCKS = 6,
+  PKV_K_COUNT = 7
 };
 
 /* Text for a status code (static storage, never NULL). */
@@ -120,6 +121,20 @@ int pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapp
 int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
                     int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                     int dtype, void* stream);
+
+/* ---- block moves between a pool and host swap space ---------------------------------
+ * For every pair i, block pairs[2i+1] of the destination arrays (dst_k, dst_v) becomes a bit copy
+ * of block pairs[2i] of the source arrays (src_k, src_v), both pools.  The arrays hold blocks of
+ * the documented pool layout (one block = n_kv_heads * head_dim * block_size elements); each is
+ * device memory or pinned host memory from hipHostMalloc (a torch tensor with pin_memory), which
+ * the kernel reads or writes over the host link.  The pairs come from pkv_swap_out (pool -> host)
+ * or pkv_swap_in (host -> pool).  Pairs with an id outside [0, src_blocks) / [0, dst_blocks) are
+ * skipped; destinations must be distinct.  Any pointer that is neither device nor pinned host
+ * memory is PKV_ERR_INVALID, checked before the launch.  pairs: int32 [n_pairs][2], device or
+ * pinned host memory. */
+int pkv_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                    int32_t dst_blocks, const int32_t* pairs, int32_t n_pairs, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t block_size, int dtype, void* stream);
 
 /* ---- device half of the on-demand append --------------------------------------
  * One decode step appends one token per batch row.  For every row i with
@@ -388,6 +403,29 @@ int pkv_fill_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32_
                           int32_t* tables, int32_t stride, int32_t pad_value, int32_t* seq_lens);
 
 int pkv_allocator_stats(const pkv_allocator* a, pkv_stats* out);
+
+/* ---- swapping sequences to host memory ---------------------------------------------
+ * Instead of evicting a sequence and recomputing its cache, its blocks can move to host memory
+ * and come back later ("Reserve for the worst case, or page", section "What this model leaves
+ * out").  The allocator manages host_blocks host slots of one block each, with their own FIFO
+ * free list (slots 0 .. host_blocks-1 initially, head first).
+ *   swap-out: every block of a device-resident sequence, in logical order, takes the next host
+ *     slot and gives the pair (device block, host slot); then the sequence's references are
+ *     dropped exactly as pkv_free drops them (a block still shared stays on the device for its
+ *     other sequences).  The sequence is then swapped out: it keeps its id and length, cannot
+ *     append or be forked, and has no block table until it is swapped back in.
+ *   swap-in: fresh device blocks are taken in logical order, giving (host slot, device block);
+ *     the host slots return, in order, to the tail of their list.  The blocks are private.
+ * Both are all or nothing: PKV_ERR_OOM (too few host slots / device blocks) changes nothing.
+ * pairs_out needs room for 2 * (the sequence's block count) ints; *n_pairs receives that count
+ * on every return, and a smaller cap is PKV_ERR_INVALID (nothing changes).  Apply the pairs with
+ * pkv_swap_blocks before the freed blocks (or host slots) are written again: launched on the
+ * stream of the later writes, stream order guarantees it.  pkv_free of a swapped-out sequence
+ * returns its host slots. */
+int pkv_allocator_set_swap_space(pkv_allocator* a, int32_t host_blocks);   /* once per allocator */
+int pkv_swap_out(pkv_allocator* a, int64_t seq_id, int32_t* pairs_out, int32_t cap, int32_t* n_pairs);
+int pkv_swap_in(pkv_allocator* a, int64_t seq_id, int32_t* pairs_out, int32_t cap, int32_t* n_pairs);
+int pkv_swap_stats(const pkv_allocator* a, int32_t* host_blocks, int32_t* host_free, int64_t* swapped_seqs);
 
 /* Reference count of a block, or -1 for an id outside the pool. */
 int32_t pkv_block_ref_count(const pkv_allocator* a, int32_t block);

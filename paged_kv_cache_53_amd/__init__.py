@@ -26,7 +26,7 @@ __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
     "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
-    "reshape_and_cache_spans", "paged_attention_decode_flat",
+    "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks",
 ]
 
 
@@ -148,6 +148,21 @@ def copy_blocks(pairs, k_pool, v_pool, stream=None) -> None:
         raise ValueError("pairs must be a contiguous int32 [n, 2] tensor")
     _check(lib().pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0], N, Hk, D, B,
                                  dtype_code(k_pool), _stream(stream)), "pkv_copy_blocks")
+
+
+def swap_blocks(pairs, src_k, src_v, dst_k, dst_v, stream=None) -> None:
+    """Block dst of (dst_k, dst_v) becomes a copy of block src of (src_k, src_v) for each (src, dst)
+    in pairs.  Each array is a device pool or pinned host swap space of the pool layout with its own
+    block count in dim 0; pairs: int32 [n, 2], device or pinned."""
+    import torch
+    Ns, Hk, D, B = _pool_dims(src_k, src_v)
+    Nd, Hk2, D2, B2 = _pool_dims(dst_k, dst_v)
+    if (Hk, D, B) != (Hk2, D2, B2) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination must hold blocks of one shape and dtype")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int32 [n, 2] tensor")
+    _check(lib().pkv_swap_blocks(_ptr(src_k), _ptr(src_v), Ns, _ptr(dst_k), _ptr(dst_v), Nd, _ptr(pairs),
+                                 pairs.shape[0], Hk, D, B, dtype_code(src_k), _stream(stream)), "pkv_swap_blocks")
 
 
 def append_slots(slot_mapping, block_tables, seq_lens, block_size: int, stream=None) -> None:
@@ -391,6 +406,31 @@ class Allocator:
         st = _lib.pkv_stats()
         _check(lib().pkv_allocator_stats(self._h, C.byref(st)), "pkv_allocator_stats")
         return {name: getattr(st, name) for name, _ in st._fields_ if name != "reserved"}
+
+    def set_swap_space(self, host_blocks: int) -> None:
+        _check(lib().pkv_allocator_set_swap_space(self._h, host_blocks), "pkv_allocator_set_swap_space")
+
+    def _swap(self, fn, seq: int, what: str):
+        n = C.c_int32(0)
+        st = fn(self._h, seq, None, 0, C.byref(n))   # a query: reports the block count, changes nothing
+        if st == PKV_ERR_NOT_FOUND:
+            _check(st, what)
+        buf = (C.c_int32 * max(2 * n.value, 2))()
+        _check(fn(self._h, seq, buf, n.value, C.byref(n)), what)
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """Moves seq to host slots; returns the (device block, host slot) copy pairs."""
+        return self._swap(lib().pkv_swap_out, seq, "pkv_swap_out")
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """Brings seq back into fresh device blocks; returns the (host slot, device block) copy pairs."""
+        return self._swap(lib().pkv_swap_in, seq, "pkv_swap_in")
+
+    def swap_stats(self) -> dict:
+        hb, hf, ns = C.c_int32(0), C.c_int32(0), C.c_int64(0)
+        _check(lib().pkv_swap_stats(self._h, C.byref(hb), C.byref(hf), C.byref(ns)), "pkv_swap_stats")
+        return {"host_blocks": hb.value, "host_free": hf.value, "swapped_seqs": ns.value}
 
     def ref_count(self, block: int) -> int:
         return int(lib().pkv_block_ref_count(self._h, block))

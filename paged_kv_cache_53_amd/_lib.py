@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 KERNEL_NAMES = {0: "reshape_and_cache", 1: "append_slots", 2: "decode_plan", 3: "decode", 4: "decode_reduce",
-                5: "copy_blocks"}
+                5: "copy_blocks", 6: "swap_blocks"}
 
 
 class pkv_stats(C.Structure):
@@ -60,6 +60,11 @@ SIGNATURES = {
     "pkv_span_pool_trim": (C.c_int, [P]),
     "pkv_span_pool_info": (C.c_int, [P, C.POINTER(pkv_span_info)]),
     "pkv_span_mapped_tokens": (I32, [P, I32]),
+    "pkv_swap_blocks": (C.c_int, [P, P, I32, P, P, I32, P, I32, I32, I32, I32, C.c_int, P]),
+    "pkv_allocator_set_swap_space": (C.c_int, [P, I32]),
+    "pkv_swap_out": (C.c_int, [P, I64, PI32, I32, PI32]),
+    "pkv_swap_in": (C.c_int, [P, I64, PI32, I32, PI32]),
+    "pkv_swap_stats": (C.c_int, [P, PI32, PI32, PI64]),
     "pkv_allocator_create": (C.c_int, [I32, I32, PI32, C.POINTER(P)]),
     "pkv_allocator_destroy": (None, [P]),
     "pkv_alloc": (C.c_int, [P, I64, I32, PI64, PI32, PI32]),

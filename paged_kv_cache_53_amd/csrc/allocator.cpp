@@ -10,6 +10,15 @@
 // shared blocks with reference counts and copy-on-write ("PagedAttention --
 // Math + Memory Model", section "Copy-on-write: sharing blocks across
 // samples").  Every operation is all-or-nothing.  Plain C++17, no HIP.
+//
+// Swapping to host memory ("Reserve for the worst case, or page", section
+// "What this model leaves out": a preempted sequence's blocks can move to host
+// memory instead of being recomputed): a fixed number of host slots with their
+// own FIFO free list; swap-out moves every block of a sequence in logical order
+// to the next host slots and drops the sequence's references as a free does;
+// swap-in takes fresh device blocks in logical order and returns the host slots
+// to the tail of their list.  Both return the copy pairs for the caller's
+// block-copy kernel.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -29,6 +38,11 @@ struct Sequence {
   int64_t len = 0;              // tokens
 };
 
+struct Swapped {
+  std::vector<int32_t> host_slots;  // logical block i -> host slot
+  int64_t len = 0;
+};
+
 }  // namespace
 
 struct pkv_allocator {
@@ -38,6 +52,17 @@ struct pkv_allocator {
   std::vector<int32_t> ref;       // sequences whose table holds the block
   std::unordered_map<int64_t, Sequence> seqs;
   int32_t shared_blocks = 0;      // blocks with ref > 1, kept current
+  int32_t num_host = -1;          // host slots (-1: no swap space yet)
+  std::deque<int32_t> host_free;  // front = next host slot handed out
+  std::unordered_map<int64_t, Swapped> swapped;
+
+  // Drops one reference of each block of s, in logical order; a block at zero rejoins the free list.
+  void release(const Sequence& s) {
+    for (int32_t b : s.blocks) {
+      dec_ref(b);
+      if (ref[b] == 0) free_list.push_back(b);
+    }
+  }
 
   void inc_ref(int32_t b) {
     if (++ref[b] == 2) ++shared_blocks;
@@ -118,7 +143,7 @@ void pkv_allocator_destroy(pkv_allocator* a) { delete a; }
 
 int pkv_alloc(pkv_allocator* a, int64_t seq_id, int32_t n_new_tokens, int64_t* slots_out,
               int32_t* cow_pair_out, int32_t* n_cow) {
-  if (!a || n_new_tokens < 0) return PKV_ERR_INVALID;
+  if (!a || n_new_tokens < 0 || a->swapped.count(seq_id)) return PKV_ERR_INVALID;
   auto it = a->seqs.find(seq_id);
   Sequence* s = it == a->seqs.end() ? nullptr : &it->second;
   const int64_t len = s ? s->len : 0;
@@ -137,7 +162,7 @@ int pkv_alloc_batch(pkv_allocator* a, const int64_t* seq_ids, int32_t n_seqs, in
   ids.reserve(static_cast<size_t>(n_seqs) * 2);
   int64_t need = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    if (!ids.insert(seq_ids[i]).second) return PKV_ERR_INVALID;
+    if (!ids.insert(seq_ids[i]).second || a->swapped.count(seq_ids[i])) return PKV_ERR_INVALID;
     auto it = a->seqs.find(seq_ids[i]);
     const Sequence* s = it == a->seqs.end() ? nullptr : &it->second;
     if ((s ? s->len : 0) + n_new_each > std::numeric_limits<int32_t>::max()) return PKV_ERR_INVALID;
@@ -167,7 +192,7 @@ int pkv_fork(pkv_allocator* a, int64_t parent, int64_t child, int32_t n_shared_t
   if (!a || n_shared_tokens < -1) return PKV_ERR_INVALID;
   auto pit = a->seqs.find(parent);
   if (pit == a->seqs.end()) return PKV_ERR_NOT_FOUND;
-  if (a->seqs.count(child)) return PKV_ERR_INVALID;
+  if (a->seqs.count(child) || a->swapped.count(child)) return PKV_ERR_INVALID;
   const int64_t plen = pit->second.len;
   const int64_t n = n_shared_tokens < 0 ? plen : n_shared_tokens;
   if (n > plen) return PKV_ERR_INVALID;
@@ -182,13 +207,80 @@ int pkv_fork(pkv_allocator* a, int64_t parent, int64_t child, int32_t n_shared_t
 
 int pkv_free(pkv_allocator* a, int64_t seq_id) {
   if (!a) return PKV_ERR_INVALID;
+  auto sw = a->swapped.find(seq_id);
+  if (sw != a->swapped.end()) {   // a swapped-out sequence gives back its host slots
+    for (int32_t h : sw->second.host_slots) a->host_free.push_back(h);
+    a->swapped.erase(sw);
+    return PKV_OK;
+  }
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ERR_NOT_FOUND;
-  for (int32_t b : it->second.blocks) {
-    a->dec_ref(b);
-    if (a->ref[b] == 0) a->free_list.push_back(b);
-  }
+  a->release(it->second);
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_allocator_set_swap_space(pkv_allocator* a, int32_t host_blocks) {
+  if (!a || host_blocks < 0 || a->num_host >= 0) return PKV_ERR_INVALID;
+  a->num_host = host_blocks;
+  for (int32_t h = 0; h < host_blocks; ++h) a->host_free.push_back(h);
+  return PKV_OK;
+}
+
+int pkv_swap_out(pkv_allocator* a, int64_t seq_id, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!a || cap < 0 || a->num_host < 0) return PKV_ERR_INVALID;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_NOT_FOUND;
+  const Sequence& s = it->second;
+  const int32_t nb = static_cast<int32_t>(s.blocks.size());
+  if (n_pairs) *n_pairs = nb;
+  if (!pairs_out || cap < nb) return PKV_ERR_INVALID;
+  if (nb > static_cast<int32_t>(a->host_free.size())) return PKV_ERR_OOM;
+  Swapped w;
+  w.len = s.len;
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t h = a->host_free.front();
+    a->host_free.pop_front();
+    pairs_out[2 * i] = s.blocks[i];
+    pairs_out[2 * i + 1] = h;
+    w.host_slots.push_back(h);
+  }
+  a->release(s);
+  a->seqs.erase(it);
+  a->swapped.emplace(seq_id, std::move(w));
+  return PKV_OK;
+}
+
+int pkv_swap_in(pkv_allocator* a, int64_t seq_id, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!a || cap < 0) return PKV_ERR_INVALID;
+  auto it = a->swapped.find(seq_id);
+  if (it == a->swapped.end()) return PKV_ERR_NOT_FOUND;
+  const Swapped& w = it->second;
+  const int32_t nb = static_cast<int32_t>(w.host_slots.size());
+  if (n_pairs) *n_pairs = nb;
+  if (!pairs_out || cap < nb) return PKV_ERR_INVALID;
+  if (nb > static_cast<int32_t>(a->free_list.size())) return PKV_ERR_OOM;
+  Sequence s;
+  s.len = w.len;
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t b = a->free_list.front();
+    a->free_list.pop_front();
+    a->ref[b] = 1;
+    s.blocks.push_back(b);
+    pairs_out[2 * i] = w.host_slots[i];
+    pairs_out[2 * i + 1] = b;
+  }
+  for (int32_t h : w.host_slots) a->host_free.push_back(h);
+  a->swapped.erase(it);
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_swap_stats(const pkv_allocator* a, int32_t* host_blocks, int32_t* host_free, int64_t* swapped_seqs) {
+  if (!a) return PKV_ERR_INVALID;
+  if (host_blocks) *host_blocks = a->num_host < 0 ? 0 : a->num_host;
+  if (host_free) *host_free = static_cast<int32_t>(a->host_free.size());
+  if (swapped_seqs) *swapped_seqs = static_cast<int64_t>(a->swapped.size());
   return PKV_OK;
 }
 

@@ -246,6 +246,59 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The address a kernel uses for p: device memory as is, pinned (registered) host memory through its
+// device mapping.  Anything else (pageable host memory, a bad pointer) is rejected before a launch.
+bool kernel_address(const void* p, const void** out) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error the query may leave
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = p;
+    return true;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    // the mapping of the allocation's base, offset to p
+    const char* host_base = static_cast<const char*>(at.hostPointer);
+    *out = static_cast<const char*>(at.devicePointer) + (static_cast<const char*>(p) - host_base);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                    int32_t dst_blocks, const int32_t* pairs, int32_t n_pairs, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t block_size, int dtype, void* stream) {
+  if (n_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || !valid_pool_dtype(dtype) || n_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0)
+    return PKV_ERR_INVALID;
+  const int64_t block_bytes = static_cast<int64_t>(n_kv_heads) * head_dim * block_size * esize(dtype);
+  if (block_bytes % 16) return PKV_ERR_UNSUPPORTED;
+  if (n_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PKV_ERR_INVALID;
+  if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(pairs, 4))
+    return PKV_ERR_INVALID;
+  const void *sk, *sv, *dk, *dv, *pp;
+  if (!kernel_address(src_k, &sk) || !kernel_address(src_v, &sv) || !kernel_address(dst_k, &dk) ||
+      !kernel_address(dst_v, &dv) || !kernel_address(pairs, &pp))
+    return PKV_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_SWAP_BLOCKS, st);
+  const hipError_t e = launch_move_blocks(sk, sv, src_blocks, const_cast<void*>(dk), const_cast<void*>(dv),
+                                          dst_blocks, static_cast<const int32_t*>(pp), n_pairs, block_bytes, st);
+  timing_after(PKV_K_SWAP_BLOCKS, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
                      int32_t block_table_stride, int32_t* seq_lens, int32_t block_size, void* stream) {
   if (num_seqs < 0 || block_table_stride <= 0 || block_size <= 0) return PKV_ERR_INVALID;

@@ -73,6 +73,10 @@ hipError_t launch_reshape_and_cache_fp8(const ScatterArgs& a, int src_dtype, flo
 // Copies whole blocks (both pools, every head) for each (src, dst) pair.
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+// Copies whole blocks (both pools) from one block array to another (device or pinned host memory).
+hipError_t launch_move_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                              int32_t dst_blocks, const int32_t* pairs, int32_t n_pairs, int64_t block_bytes,
+                              hipStream_t stream);
 hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* block_tables,
                                int32_t stride, int32_t* seq_lens, int32_t block_size,
                                hipStream_t stream);

@@ -135,16 +135,21 @@ __global__ __launch_bounds__(256) void append_slots_kernel(const int64_t* __rest
   seq_lens[i] = p + 1;
 }
 
-// Copy-on-write: block dst of a pool becomes a copy of block src.  Grid: (pair, pool, slice);
-// each workgroup moves one slice of one block with 16-byte loads and stores.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(void* k_pool, void* v_pool, const int32_t* pairs,
-                                                          int32_t num_blocks, int64_t block_bytes) {
+// Block copies between two block arrays (the same pool for copy-on-write; a device pool and host
+// swap space for swapping): block dst of the destination becomes a copy of block src of the source.
+// Grid: (pair, pool, slice); each workgroup moves one slice of one block with 16-byte loads and
+// stores.  Either array may be pinned host memory, reached over the host link.
+__global__ __launch_bounds__(256) void move_blocks_kernel(const void* src_k, const void* src_v, void* dst_k,
+                                                          void* dst_v, const int32_t* pairs, int32_t src_blocks,
+                                                          int32_t dst_blocks, int64_t block_bytes) {
   const int src = pairs[2 * static_cast<int64_t>(blockIdx.x)];
   const int dst = pairs[2 * static_cast<int64_t>(blockIdx.x) + 1];
-  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
-  char* pool = static_cast<char*>(blockIdx.y ? v_pool : k_pool);
-  const uint4* s = reinterpret_cast<const uint4*>(pool + src * block_bytes);
-  uint4* d = reinterpret_cast<uint4*>(pool + dst * block_bytes);
+  if (src < 0 || dst < 0 || src >= src_blocks || dst >= dst_blocks) return;
+  if (src == dst && (blockIdx.y ? src_v == dst_v : src_k == dst_k)) return;   // a block onto itself
+  const char* sp = static_cast<const char*>(blockIdx.y ? src_v : src_k);
+  char* dp = static_cast<char*>(blockIdx.y ? dst_v : dst_k);
+  const uint4* s = reinterpret_cast<const uint4*>(sp + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(dp + dst * block_bytes);
   const int64_t vecs = block_bytes / 16;
   for (int64_t i = static_cast<int64_t>(blockIdx.z) * blockDim.x + threadIdx.x; i < vecs;
        i += static_cast<int64_t>(gridDim.z) * blockDim.x)
@@ -153,14 +158,21 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(void* k_pool, void* v_
 
 }  // namespace
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
-                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+hipError_t launch_move_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                              int32_t dst_blocks, const int32_t* pairs, int32_t n_pairs, int64_t block_bytes,
+                              hipStream_t stream) {
   if (n_pairs == 0) return hipSuccess;
   // slices of at least 4 KiB per workgroup, at most 8 per block
   const int64_t slices = std::min<int64_t>(8, std::max<int64_t>(1, block_bytes / 4096));
-  copy_blocks_kernel<<<dim3(static_cast<unsigned>(n_pairs), 2, static_cast<unsigned>(slices)), dim3(256), 0,
-                       stream>>>(k_pool, v_pool, pairs, num_blocks, block_bytes);
+  move_blocks_kernel<<<dim3(static_cast<unsigned>(n_pairs), 2, static_cast<unsigned>(slices)), dim3(256), 0,
+                       stream>>>(src_k, src_v, dst_k, dst_v, pairs, src_blocks, dst_blocks, block_bytes);
   return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  return launch_move_blocks(k_pool, v_pool, num_blocks, k_pool, v_pool, num_blocks, pairs, n_pairs, block_bytes,
+                            stream);
 }
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream) {

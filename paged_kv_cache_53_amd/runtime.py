@@ -2,6 +2,8 @@
 
 PagedKVCache   one layer's key/value pools on the device and the host block allocator that
                hands out their slots (prompt writes go allocator -> scatter kernel).  With
+               enable_swap(host_blocks) it also keeps pinned host swap space, and swap_out /
+               swap_in move a sequence's blocks there and back (allocator pairs -> copy kernel).  With
                dtype torch.float8_e4m3fn the pools hold FP8 E4M3 codes under the per-tensor
                scales k_scale / v_scale (the scatter quantises, decode reads the scaled values).
 DecodeBatch    a fixed set of sequences decoded together: device block tables and lengths,
@@ -29,8 +31,8 @@ import numpy as np
 import torch
 
 from . import (Allocator, SpanPool, append_slots, copy_blocks, key_pool_shape, paged_attention_decode,
-               paged_attention_decode_flat, reshape_and_cache, reshape_and_cache_spans, value_pool_shape,
-               workspace_size)
+               paged_attention_decode_flat, reshape_and_cache, reshape_and_cache_spans, swap_blocks,
+               value_pool_shape, workspace_size)
 
 
 class PagedKVCache:
@@ -88,6 +90,31 @@ class PagedKVCache:
     def fork(self, parent: int, child: int, n_tokens: int = -1) -> None:
         self.allocator.fork(parent, child, n_tokens)
 
+    def enable_swap(self, host_blocks: int) -> None:
+        """Pinned host swap space of host_blocks blocks (both pools), managed by the allocator."""
+        self.allocator.set_swap_space(host_blocks)
+        ks = key_pool_shape(host_blocks, self.n_kv_heads, self.head_dim, self.block_size, self.dtype)
+        vs = value_pool_shape(host_blocks, self.n_kv_heads, self.head_dim, self.block_size)
+        self.k_host = torch.empty(ks, dtype=self.dtype, pin_memory=True)
+        self.v_host = torch.empty(vs, dtype=self.dtype, pin_memory=True)
+
+    def swap_out(self, seq: int) -> int:
+        """Moves seq's blocks to host memory (copies issued on the current stream, before anything
+        later can reuse the freed blocks); returns the number of blocks moved."""
+        pairs = self.allocator.swap_out(seq)
+        if pairs:
+            swap_blocks(torch.tensor(pairs, dtype=torch.int32, device=self.device), self.k_pool, self.v_pool,
+                        self.k_host, self.v_host)
+        return len(pairs)
+
+    def swap_in(self, seq: int) -> int:
+        """Brings seq back into fresh device blocks (its block table changes)."""
+        pairs = self.allocator.swap_in(seq)
+        if pairs:
+            swap_blocks(torch.tensor(pairs, dtype=torch.int32, device=self.device), self.k_host, self.v_host,
+                        self.k_pool, self.v_pool)
+        return len(pairs)
+
     def free(self, seq: int) -> None:
         self.allocator.free(seq)
 
@@ -141,6 +168,14 @@ class DecodeBatch:
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
                                shared_kv=c.has_shared_blocks(), **c.scales)
         self.steps += 1
+
+    def refresh(self) -> None:
+        """Reloads the device tables and lengths from the allocator (after a row was swapped back in,
+        its blocks differ)."""
+        tables, lens = self.cache.allocator.fill_block_tables(self.seq_ids, self.stride, pad=0)
+        self.tables.copy_(torch.from_numpy(tables))
+        self.seq_lens.copy_(torch.from_numpy(lens.copy()))
+        self.host_lens = lens.astype(np.int64)
 
     def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
         """Attention over the current tokens without appending (no host work, no scatter)."""

@@ -76,6 +76,75 @@ def test_matches_model_under_random_ops(ops, B, N, seed):
         same_state(model, lib)
 
 
+def apply_swap_ops(model, lib, kind, x, y, n):
+    """The swap operations on both sides (plus the others); compares pairs and errors."""
+    if kind not in ("swap_out", "swap_in"):
+        return apply_both(model, lib, kind, x, y, n)
+    err_m = err_l = None
+    res_m = res_l = None
+    try:
+        res_m = model.swap_out(x) if kind == "swap_out" else model.swap_in(x)
+    except OutOfBlocks:
+        err_m = "oom"
+    except KeyError:
+        err_m = "missing"
+    try:
+        res_l = lib.swap_out(x) if kind == "swap_out" else lib.swap_in(x)
+    except pkv.PKVError as e:
+        err_l = {pkv.PKV_ERR_OOM: "oom", pkv.PKV_ERR_NOT_FOUND: "missing", pkv.PKV_ERR_INVALID: "invalid"}[e.status]
+    assert err_m == err_l, (kind, x, err_m, err_l)
+    if err_m is None:
+        assert [tuple(p) for p in res_l] == [tuple(p) for p in res_m]
+
+
+def same_swap_state(model, lib):
+    same_state(model, lib)
+    st = lib.swap_stats()
+    assert st["host_free"] == len(model.host_free) and st["swapped_seqs"] == len(model.swapped)
+
+
+swap_ops = st.lists(st.tuples(st.sampled_from(["alloc", "alloc", "alloc", "fork", "free", "swap_out", "swap_in",
+                                               "swap_in"]),
+                              st.integers(0, 6), st.integers(0, 6), st.integers(-1, 45)), max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=swap_ops, B=st.sampled_from([1, 4, 16]), N=st.integers(1, 30), H=st.integers(0, 20),
+       seed=st.integers(0, 10 ** 6))
+def test_swaps_match_model_under_random_ops(ops, B, N, H, seed):
+    order = np.random.default_rng(seed).permutation(N).tolist()
+    model, lib = BlockAllocatorModel(N, B, order), pkv.Allocator(N, B, order)
+    model.set_swap_space(H)
+    lib.set_swap_space(H)
+    for kind, x, y, n in ops:
+        if kind == "alloc":
+            n = max(n, 0)
+        apply_swap_ops(model, lib, kind, x, y, n)
+        same_swap_state(model, lib)
+
+
+def test_swap_requires_swap_space_and_reports_the_block_count():
+    import ctypes as C
+    lib = pkv.Allocator(8, 4)
+    lib.alloc(0, 10)
+    with pytest.raises(pkv.PKVError):
+        lib.swap_out(0)                              # no swap space yet
+    lib.set_swap_space(4)
+    with pytest.raises(pkv.PKVError):
+        lib.set_swap_space(4)                        # set once
+    table = lib.block_table(0)
+    n = C.c_int32(0)
+    small = (C.c_int32 * 2)()
+    assert pkv.lib().pkv_swap_out(lib._h, 0, small, 1, C.byref(n)) == pkv.PKV_ERR_INVALID
+    assert n.value == 3 and lib.block_table(0) == table   # too small: nothing changed, count reported
+    assert lib.swap_out(0) == [(b, h) for h, b in enumerate(table)]
+    assert lib.free_list()[-3:] == table
+    with pytest.raises(pkv.PKVError):
+        lib.alloc(0, 1)                              # swapped out: cannot append
+    with pytest.raises(pkv.PKVError):
+        lib.block_table(0)                           # and has no table
+
+
 @pytest.mark.parametrize("cid,copied", [(1, False), (2, False), (3, False), (4, False), (4, True), (5, False)])
 def test_workload_scripts_give_identical_tables(cid, copied):
     w = wl.build(cid, small=True, copied_prefix=copied) if cid == 4 else wl.build(cid, small=True)
