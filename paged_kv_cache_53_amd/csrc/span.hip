@@ -132,7 +132,7 @@ int pkv_span_pool_create(int32_t max_spans, int32_t max_tokens, int32_t n_kv_hea
   const size_t block_bytes = static_cast<size_t>(n_kv_heads) * head_dim * block_size * es;
   // a span is a whole number of chunks and of blocks
   const size_t unit = std::lcm(chunk, block_bytes);
-  const size_t want = static_cast<size_t>((max_tokens + block_size - 1) / block_size) * block_bytes;
+  const size_t want = static_cast<size_t>((static_cast<int64_t>(max_tokens) + block_size - 1) / block_size) * block_bytes;
   const size_t span_bytes = (want + unit - 1) / unit * unit;
   const size_t bps = span_bytes / block_bytes;
   if (bps > (size_t{1} << 30) || bps * static_cast<size_t>(max_spans) >= (size_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
@@ -144,13 +144,14 @@ int pkv_span_pool_create(int32_t max_spans, int32_t max_tokens, int32_t n_kv_hea
   p->block_bytes = block_bytes;
   p->span_bytes = span_bytes;
   p->chunk_bytes = chunk;
+  for (int k = 0; k < 2; ++k) p->mapped[k].assign(max_spans, {});   // before any failure path walks them
   for (int k = 0; k < 2; ++k) {
     if (hipMemAddressReserve(&p->va[k], span_bytes * static_cast<size_t>(max_spans), chunk, nullptr, 0) != hipSuccess) {
+      p->va[k] = nullptr;
       destroy_all(p);
       delete p;
       return PKV_ERR_OOM;
     }
-    p->mapped[k].assign(max_spans, {});
   }
   *out = p;
   return PKV_OK;
