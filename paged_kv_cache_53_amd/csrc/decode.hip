@@ -85,6 +85,28 @@ __device__ inline float lane_fetch(float v, int src) {
 
 __device__ inline float xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Symmetric reductions with lane ^ 16 and lane ^ 32 through the gfx950 row and half swaps
+// (v_permlane16_swap / v_permlane32_swap), which exchange inside the VALU instead of through LDS as a
+// shuffle does.  With both operands equal, each lane gets its own value and its partner's, in an
+// order that depends on the lane; a maximum or a sum of the two is the same either way (IEEE
+// addition is commutative, so sums are bit-identical to the shuffle form).
+__device__ inline float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T> __device__ inline float to_f32(T x) { return static_cast<float>(x); }
 
 // Finished results (outputs and partials) are written through to memory (the sc1 policy).  A
@@ -583,8 +605,7 @@ struct MfmaMath {
         if (t0 + 4 * g + i >= ntok) x[i] = -INFINITY;
     }
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, xor_f(mt, 16));
-    mt = fmaxf(mt, xor_f(mt, 32));
+    mt = max_x32(max_x16(mt));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -643,8 +664,7 @@ struct MfmaMath {
         if (t0 + 8 * g + i >= ntok) x[i] = -INFINITY;
     }
     float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mt = fmaxf(mt, xor_f(mt, 16));
-    mt = fmaxf(mt, xor_f(mt, 32));
+    mt = max_x32(max_x16(mt));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -676,8 +696,7 @@ struct MfmaMath {
   // quantised values the accumulator is scaled by the value scale
   __device__ void finish(const DecodeArgs& a, const Unit<KV>& u) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
-    float l_tot = l_run + xor_f(l_run, 16);
-    l_tot += xor_f(l_tot, 32);
+    const float l_tot = sum_x32(sum_x16(l_run));
     if (r16 >= a.group) return;
     const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + r16;
     if (u.nparts == 1) {
@@ -755,8 +774,7 @@ struct VecMath {
 #pragma unroll
         for (int e = 0; e < X; ++e) dot = fmaf(qv[e], kv[ks][e], dot);
       }
-      dot += xor_f(dot, 16);
-      dot += xor_f(dot, 32);
+      dot = sum_x32(sum_x16(dot));
       float xs = dot * scale_log2;
       if (partial && t0 + r16 >= ntok) xs = -INFINITY;
       float mt = fmaxf(xs, xor_f(xs, 1));
@@ -791,8 +809,7 @@ struct VecMath {
       float o[D / 16];
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        float v = acc[gi][dt] + xor_f(acc[gi][dt], 16);
-        o[dt] = v + xor_f(v, 32);
+        o[dt] = sum_x32(sum_x16(acc[gi][dt]));
       }
       if (g != 0) continue;
       const int64_t row = static_cast<int64_t>(u.s) * a.n_q_heads + u.kvh * a.group + gi;
