@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--sweep", action="store_true", help="config-5 block-size x placement sweep (decode only)")
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
+    p.add_argument("--unfused", action="store_true",
+                   help="paged steps as separate calls (slot copy, append_slots, scatter, decode) instead of "
+                        "one decode_step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     p.add_argument("--copy-blocks", action="store_true",
@@ -134,7 +137,7 @@ def kv_bytes(w, lens, table=True):
 
 
 # ------------------------------------------------------------------------------------- GPU timing
-def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0):
+def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True):
     import numpy as np
     import torch
 
@@ -151,6 +154,8 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
     def one():
         if decode_only:
             batch.decode_only(q, out)
+        elif layout == "paged":
+            batch.step(q, kn, vn, out, fused=fused)
         else:
             batch.step(q, kn, vn, out)
 
@@ -387,6 +392,16 @@ def _oracle_sample(w, budget_s, cores, used):
 
 
 # ------------------------------------------------------------------------------------- main
+def step_description(args):
+    if args.decode_only:
+        return "decode_only"
+    if args.layout == "flat":
+        return "host append + span mapping + stage + append_slots + scatter + decode"
+    if args.unfused:
+        return "host append + slot copy + append_slots + scatter + decode (plan, attention, merge)"
+    return "host append + decode_step (prologue: append_slots + plan + scatter; attention; merge)"
+
+
 def make_workload(args):
     import workloads as wl
     w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
@@ -429,7 +444,7 @@ def main():
 
     w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
-                     chunk_bytes=args.chunk_bytes)
+                     chunk_bytes=args.chunk_bytes, fused=not args.unfused)
     total_s = res["total_s"]
     gbps = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
     seqs_s = w.num_seqs * args.steps / total_s
@@ -445,8 +460,7 @@ def main():
                    "kv_dtype": "fp8_e4m3 (per-tensor scales)" if w.kv_format == "fp8" else w.dtype,
                    "layout": "paged" if args.layout == "paged" else
                    f"flat spans ({args.chunk_bytes or 2 << 20}-byte chunks, no block table)",
-                   "seed": w.seed, "step": "decode_only" if args.decode_only else
-                   "host append + stage + append_slots + scatter + decode"},
+                   "seed": w.seed, "step": step_description(args)},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(seqs_s, 1),
         "kernels": kern,

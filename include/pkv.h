@@ -65,7 +65,8 @@ enum {
   PKV_K_DECODE_REDUCE = 4,
   PKV_K_COPY_BLOCKS = 5,
   PKV_K_SWAP_BLOCKS = 6,
-  PKV_K_COUNT = 7
+  PKV_K_STEP_PROLOGUE = 7,
+  PKV_K_COUNT = 8
 };
 
 /* Text for a status code (static storage, never NULL). */
@@ -257,6 +258,66 @@ int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int 
                                    int32_t num_blocks, float scale, int32_t max_seq_len,
                                    int32_t partition_size, void* workspace, size_t workspace_bytes,
                                    uint32_t flags, void* stream);
+
+/* ---- a whole decode step in fewer launches -----------------------------------------------------
+ * One decode step of a batch: every row appends one token and attends over all of its tokens
+ * ("PagedAttention -- Math + Memory Model", section "PagedAttention: blocks and the block table":
+ * the new token's key and value go to its slot, its block is recorded in the row's table, and the
+ * attention then reads every token through the table).  The result is exactly that of
+ *   pkv_append_slots(slot_mapping, ...);
+ *   pkv_reshape_and_cache(k, v, slot_mapping, num_tokens = num_seqs, ...)   (kv_fp8: _fp8);
+ *   pkv_paged_attention_decode_ex(...)                                       (kv_fp8: _fp8);
+ * on one stream: the same bits in the pools, the block tables, the lengths and the output.  It runs
+ * as one prologue kernel (one workgroup appends and then plans the attention's work over the new
+ * lengths while the others scatter), the attention kernel and, when a row spans more than one
+ * partition, the merge: three fewer launches than the separate calls.
+ *   slot_mapping   int64 [num_seqs]: the slot of row s's new token (token s of k and v), as the
+ *                  allocator gave it; a negative slot skips the row's scatter and append.  Device
+ *                  memory or pinned host memory (hipHostMalloc): the prologue reads
+ *                  host memory over the host link, once per token, so the step needs no copy.
+ *                  It must not change until the prologue has run.  Pageable host memory:
+ *                  PKV_ERR_INVALID.
+ *   k, v           device rows, token s of each at s * k_token_stride (v_token_stride) elements of
+ *                  dtype, n_kv_heads * head_dim elements each; strides 0 = packed; 16-byte aligned
+ *   kv_fp8         0: the pools hold dtype; 1: they hold FP8 E4M3 codes under k_scale / v_scale
+ *                  (dtype PKV_F16 or PKV_BF16)
+ *   block_tables, seq_lens  device, updated by the append and then read by the attention
+ *   dtype          the type of k, v and q (and of out unless out_dtype is PKV_F32)
+ * Every other field as for pkv_paged_attention_decode_ex / pkv_paged_attention_decode_fp8.  The
+ * checks are those of the three calls; a rejected step changes nothing. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t k_token_stride;
+  int64_t v_token_stride;
+  const int64_t* slot_mapping;
+  void* k_pool;
+  void* v_pool;
+  int32_t num_blocks;
+  int32_t kv_fp8;
+  float k_scale;
+  float v_scale;
+  int32_t* block_tables;
+  int32_t* seq_lens;
+  int32_t block_table_stride;
+  int32_t num_seqs;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  void* out;
+  int32_t out_dtype;
+  int32_t dtype;
+  const void* q;
+  float scale;
+  int32_t max_seq_len;
+  int32_t partition_size;
+  uint32_t flags;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_decode_step_args;
+
+int pkv_decode_step(const pkv_decode_step_args* args, void* stream);
 
 /* ---- flat spans: contiguous virtual ranges backed on demand ------------------------------
  * The alternative to a block table that "Contiguous vs Paged KV Cache on RDNA4" names (sections

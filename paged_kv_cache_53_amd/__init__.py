@@ -12,6 +12,9 @@ nothing falls back if the library is missing.
 A quantised cache has pools of torch.float8_e4m3fn (or uint8) holding FP8 E4M3 codes, one
 per-tensor scale per pool: pass k_scale / v_scale to reshape_and_cache and
 paged_attention_decode.
+
+decode_step(out, q, k, v, slot_mapping, k_pool, v_pool, block_tables, seq_lens, ...) is one decode
+step (the device append, the scatter and the attention) in fewer launches, with the same results.
 """
 from __future__ import annotations
 
@@ -26,7 +29,7 @@ __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
     "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
-    "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks",
+    "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks", "decode_step",
 ]
 
 
@@ -218,6 +221,51 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
         dtype_code(k_pool), flags, _stream(stream)),
         "pkv_paged_attention_decode_ex")
+
+
+def decode_step(out, q, k, v, slot_mapping, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                max_seq_len: int, partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False,
+                k_scale=None, v_scale=None) -> None:
+    """One decode step: append_slots, reshape_and_cache and paged_attention_decode with the same
+    results, in fewer launches (pkv_decode_step).  Row s appends token s of k / v ([S, Hk, D], token
+    rows may be strided) at slot_mapping[s]; slot_mapping is int64 [S] on the device or in pinned
+    host memory (read by the kernel in place).  Other arguments as for paged_attention_decode."""
+    import torch
+    N, Hk, D, B = _pool_dims(k_pool, v_pool)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [S, Hq, D]")
+    if k.shape != (S, Hk, D) or v.shape != (S, Hk, D) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [S, Hk, D] of q's dtype")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError("k/v rows must be contiguous within a token")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (S,) or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 [S] tensor")
+    if not slot_mapping.is_cuda and not slot_mapping.is_pinned():
+        raise ValueError("a host slot_mapping must be in pinned memory")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [S, stride] with unit column stride")
+    fp8 = _is_fp8_pool(k_pool)
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("an FP8 cache needs k_scale and v_scale")
+    if not fp8 and (k_scale is not None or v_scale is not None):
+        raise ValueError("scales apply to FP8 pools only")
+    if not fp8 and k_pool.dtype != q.dtype:
+        raise ValueError("the pools must hold q's dtype (or FP8 codes)")
+    need = workspace_size(S, Hq, D, max_seq_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    a = _lib.pkv_decode_step_args(
+        k=_ptr(k), v=_ptr(v), k_token_stride=k.stride(0), v_token_stride=v.stride(0),
+        slot_mapping=_ptr(slot_mapping), k_pool=_ptr(k_pool), v_pool=_ptr(v_pool), num_blocks=N,
+        kv_fp8=1 if fp8 else 0, k_scale=float(k_scale) if fp8 else 1.0, v_scale=float(v_scale) if fp8 else 1.0,
+        block_tables=_ptr(block_tables), seq_lens=_ptr(seq_lens), block_table_stride=block_tables.stride(0),
+        num_seqs=S, n_q_heads=Hq, n_kv_heads=Hk, head_dim=D, block_size=B, out=_ptr(out),
+        out_dtype=dtype_code(out), dtype=dtype_code(q), q=_ptr(q), scale=float(scale), max_seq_len=int(max_seq_len),
+        partition_size=int(partition_size), flags=PKV_DECODE_SHARED_KV if shared_kv else 0,
+        workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check(lib().pkv_decode_step(C.byref(a), _stream(stream)), "pkv_decode_step")
 
 
 class SpanPool:

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 KERNEL_NAMES = {0: "reshape_and_cache", 1: "append_slots", 2: "decode_plan", 3: "decode", 4: "decode_reduce",
-                5: "copy_blocks", 6: "swap_blocks"}
+                5: "copy_blocks", 6: "swap_blocks", 7: "step_prologue"}
 
 
 class pkv_stats(C.Structure):
@@ -23,6 +23,18 @@ class pkv_span_info(C.Structure):
     _fields_ = [("k_base", C.c_void_p), ("v_base", C.c_void_p), ("blocks_per_span", C.c_int32),
                 ("num_blocks", C.c_int32), ("chunk_bytes", C.c_size_t), ("span_bytes", C.c_size_t),
                 ("mapped_bytes", C.c_size_t), ("spare_bytes", C.c_size_t)]
+
+
+class pkv_decode_step_args(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("k_token_stride", C.c_int64),
+                ("v_token_stride", C.c_int64), ("slot_mapping", C.c_void_p), ("k_pool", C.c_void_p),
+                ("v_pool", C.c_void_p), ("num_blocks", C.c_int32), ("kv_fp8", C.c_int32), ("k_scale", C.c_float),
+                ("v_scale", C.c_float), ("block_tables", C.c_void_p), ("seq_lens", C.c_void_p),
+                ("block_table_stride", C.c_int32), ("num_seqs", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
+                ("out", C.c_void_p), ("out_dtype", C.c_int32), ("dtype", C.c_int32), ("q", C.c_void_p),
+                ("scale", C.c_float), ("max_seq_len", C.c_int32), ("partition_size", C.c_int32),
+                ("flags", C.c_uint32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
 class pkv_kernel_time(C.Structure):
@@ -53,6 +65,7 @@ SIGNATURES = {
                                                  C.c_uint32, P]),
     "pkv_paged_attention_decode_flat": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                                   C.c_float, I32, I32, P, SZ, C.c_int, C.c_uint32, P]),
+    "pkv_decode_step": (C.c_int, [C.POINTER(pkv_decode_step_args), P]),
     "pkv_span_pool_create": (C.c_int, [I32, I32, I32, I32, I32, C.c_int, SZ, C.POINTER(P)]),
     "pkv_span_pool_destroy": (None, [P]),
     "pkv_span_reserve": (C.c_int, [P, I32, I32]),

@@ -1,5 +1,6 @@
 // C-ABI entry points of libpagedkv: argument checks, workspace carve-up, kernel dispatch,
 // and the optional per-kernel event timing.  Every check runs before anything is launched.
+#include <cmath>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -339,15 +340,26 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
 
 namespace {
 
-// Every decode entry point.  q_dtype: the type of q (and of out unless out is fp32); kv_fp8: the
-// pools hold E4M3 codes with scales k_scale / v_scale (else they hold q_dtype); flat_bps > 0: flat
-// spans of flat_bps blocks, block_tables then holds one span index per row.
-int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
-                bool kv_fp8, float k_scale, float v_scale, const int32_t* block_tables,
-                int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
-                int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                uint32_t flags, void* stream, int32_t flat_bps = 0) {
+// A checked decode call, ready to launch.
+struct DecodeLaunch {
+  DecodeArgs a;
+  int kv_dtype, head_dim, path;
+  bool kv_fp8, nt;
+  int32_t grid;
+  bool empty;   // no rows: nothing to launch
+};
+
+// Every check of a decode call, then its kernel arguments.  q_dtype: the type of q (and of out
+// unless out is fp32); kv_fp8: the pools hold E4M3 codes with scales k_scale / v_scale (else they
+// hold q_dtype); flat_bps > 0: flat spans of flat_bps blocks, block_tables then holds one span
+// index per row.
+int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool,
+                   const void* v_pool, bool kv_fp8, float k_scale, float v_scale, const int32_t* block_tables,
+                   int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                   int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                   int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                   uint32_t flags, int32_t flat_bps = 0) {
+  L->empty = false;
   const int kv_dtype = q_dtype;   // the compute type of the kernels
   const bool flat = flat_bps > 0;
   if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV)) return PKV_ERR_INVALID;
@@ -357,7 +369,7 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
   if (num_seqs < 0 || n_q_heads <= 0 || n_q_heads > 65535 || n_kv_heads <= 0 || (n_q_heads % n_kv_heads) ||
       num_blocks <= 0 ||
       max_seq_len < 0 || partition_size < 0 || (partition_size % 32) || block_size <= 0 ||
-      !(scale == scale))
+      !std::isfinite(scale))
     return PKV_ERR_INVALID;
   if (block_size != 8 && block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -382,7 +394,10 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
   const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
   const int64_t unit_bound = static_cast<int64_t>(num_seqs) * max_parts * n_kv_heads;
   if (unit_bound >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs == 0) {
+    L->empty = true;
+    return PKV_OK;
+  }
   // ---- pointer checks
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens || !workspace) return PKV_ERR_INVALID;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
@@ -392,7 +407,8 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
   if (workspace_bytes < wl.total) return PKV_ERR_INVALID;
 
   char* ws = static_cast<char*>(workspace);
-  DecodeArgs a{};
+  DecodeArgs& a = L->a;
+  a = DecodeArgs{};
   a.out = out;
   a.q = q;
   a.k_pool = k_pool;
@@ -422,24 +438,53 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
 
   int32_t cap = 0;
   if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
-  const int32_t grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
+  L->grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
+  L->kv_dtype = kv_dtype;
+  L->head_dim = head_dim;
+  L->path = path;
+  L->kv_fp8 = kv_fp8;
+  L->nt = (flags & PKV_DECODE_SHARED_KV) == 0;
+  return PKV_OK;
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  timing_before(PKV_K_DECODE_PLAN, st);
-  hipError_t e = launch_decode_plan(a, kv_dtype, head_dim, st);
-  timing_after(PKV_K_DECODE_PLAN, st);
-  if (e != hipSuccess) return PKV_ERR_HIP;
+// The launches of a prepared decode: the plan (unless a fused step's prologue made it), the
+// attention kernel, and the merge where some row has more than one partition.
+int decode_launch(const DecodeLaunch& L, bool plan, hipStream_t st) {
+  if (L.empty) return PKV_OK;
+  const DecodeArgs& a = L.a;
+  hipError_t e;
+  if (plan) {
+    timing_before(PKV_K_DECODE_PLAN, st);
+    e = launch_decode_plan(a, L.kv_dtype, L.head_dim, st);
+    timing_after(PKV_K_DECODE_PLAN, st);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  }
   timing_before(PKV_K_DECODE, st);
-  e = launch_decode_main(a, kv_dtype, kv_fp8, head_dim, path, (flags & PKV_DECODE_SHARED_KV) == 0, grid, st);
+  e = launch_decode_main(a, L.kv_dtype, L.kv_fp8, L.head_dim, L.path, L.nt, L.grid, st);
   timing_after(PKV_K_DECODE, st);
   if (e != hipSuccess) return PKV_ERR_HIP;
-  if (max_parts > 1) {
+  if (a.max_parts > 1) {
     timing_before(PKV_K_DECODE_REDUCE, st);
-    e = launch_decode_reduce(a, kv_dtype, head_dim, st);
+    e = launch_decode_reduce(a, L.kv_dtype, L.head_dim, st);
     timing_after(PKV_K_DECODE_REDUCE, st);
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                bool kv_fp8, float k_scale, float v_scale, const int32_t* block_tables,
+                int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                uint32_t flags, void* stream, int32_t flat_bps = 0) {
+  DecodeLaunch L;
+  const int r = decode_prepare(&L, out, out_dtype, q, q_dtype, k_pool, v_pool, kv_fp8, k_scale, v_scale, block_tables,
+                               block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size,
+                               num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags,
+                               flat_bps);
+  if (r != PKV_OK) return r;
+  return decode_launch(L, true, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -479,6 +524,46 @@ int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int 
   return decode_impl(out, out_dtype, q, q_dtype, k_pool, v_pool, true, k_scale, v_scale, block_tables,
                      block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size,
                      num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags, stream);
+}
+
+int pkv_decode_step(const pkv_decode_step_args* p, void* stream) {
+  if (!p) return PKV_ERR_INVALID;
+  // ---- the scatter's checks (one new token per row, rows of dtype)
+  const int dtype = p->dtype;
+  if (!valid_dtype(dtype) || (p->kv_fp8 != 0 && p->kv_fp8 != 1)) return PKV_ERR_INVALID;
+  const bool fp8 = p->kv_fp8 == 1;
+  if (p->num_seqs < 0 || p->n_kv_heads <= 0 || p->head_dim <= 0) return PKV_ERR_INVALID;
+  const int es = esize(dtype);
+  if (p->head_dim % (fp8 ? 16 : 16 / es)) return PKV_ERR_INVALID;
+  const int64_t row = static_cast<int64_t>(p->n_kv_heads) * p->head_dim;
+  const int64_t ks = p->k_token_stride == 0 ? row : p->k_token_stride;
+  const int64_t vs = p->v_token_stride == 0 ? row : p->v_token_stride;
+  if (ks < row || vs < row || (ks * es) % 16 || (vs * es) % 16) return PKV_ERR_INVALID;
+  if (p->num_seqs > 0) {   // the new rows and the slot mapping (an empty step reads neither)
+    if (!p->k || !p->v || !aligned(p->k, 16) || !aligned(p->v, 16)) return PKV_ERR_INVALID;
+    if (!p->slot_mapping || !aligned(p->slot_mapping, 8) || p->block_table_stride <= 0) return PKV_ERR_INVALID;
+  }
+  // ---- the decode's checks (the append's are among them: positive block size, a table stride that
+  // holds max_seq_len tokens), then its kernel arguments
+  DecodeLaunch L;
+  const int r = decode_prepare(&L, p->out, p->out_dtype, p->q, dtype, p->k_pool, p->v_pool, fp8, p->k_scale,
+                               p->v_scale, p->block_tables, p->block_table_stride, p->seq_lens, p->num_seqs,
+                               p->n_q_heads, p->n_kv_heads, p->head_dim, p->block_size, p->num_blocks, p->scale,
+                               p->max_seq_len, p->partition_size, p->workspace, p->workspace_bytes, p->flags);
+  if (r != PKV_OK) return r;
+  if (L.empty) return PKV_OK;
+  const void* slots = nullptr;
+  if (!kernel_address(p->slot_mapping, &slots)) return PKV_ERR_INVALID;   // pageable host memory, or no memory
+  ScatterArgs sc{p->k, p->v, static_cast<const int64_t*>(slots), p->k_pool, p->v_pool, ks, vs, p->num_seqs,
+                 p->num_blocks, p->n_kv_heads, p->head_dim, p->block_size};
+  StepArgs sa{static_cast<const int64_t*>(slots), p->block_tables, p->seq_lens, fp8 ? p->k_scale : 1.f,
+              fp8 ? p->v_scale : 1.f};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_before(PKV_K_STEP_PROLOGUE, st);
+  const hipError_t e = launch_step_prologue(L.a, sc, sa, dtype, fp8, p->head_dim, st);
+  timing_after(PKV_K_STEP_PROLOGUE, st);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return decode_launch(L, false, st);
 }
 
 int pkv_timing_enable(int enable) {

@@ -55,6 +55,7 @@
 #include <type_traits>
 
 #include "pkv_internal.h"
+#include "scatter_body.h"
 
 namespace pkv {
 namespace {
@@ -197,8 +198,10 @@ __device__ inline int block_scan_1024(int v, int* wave_sums, int* total) {
 // shorter last partition in decreasing length (counting sort over 16-token buckets).  Waves
 // claim units in this order, so the last units handed out are the shortest and the waves
 // finish together.  The order decides only which wave computes a unit, never its result.
-template <typename T>
-__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int head_dim) {
+// Run by one workgroup of 1024 threads; thread t reads the lengths of rows t*per .. t*per+per-1
+// only (len_of(s): row s's length, clamped to 0 .. max_seq_len), in two passes.
+template <typename T, class LenOf>
+__device__ inline void plan_units(const DecodeArgs& a, int head_dim, LenOf len_of) {
   constexpr int NBUCKET = 1024;
   __shared__ int wave_sums[16];
   __shared__ int bucket_base[NBUCKET];
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
   __syncthreads();
   int full_local = 0;
   for (int s = lo; s < hi; ++s) {
-    const int L = row_len(a, s);
+    const int L = len_of(s);
     full_local += L / P;
     if (L % P) atomicAdd(&bucket_fill[((L % P) - 1) >> shift], 1);
   }
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
   __syncthreads();
   const int64_t row_elems = static_cast<int64_t>(a.n_q_heads) * head_dim;
   for (int s = lo; s < hi; ++s) {
-    const int L = row_len(a, s);
+    const int L = len_of(s);
     const int nfull = L / P;
     for (int p = 0; p < nfull; ++p) a.units[off + p] = make_int2(s, p);
     off += nfull;
@@ -246,6 +249,65 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int hea
     }
   }
   if (tid >= 1 && tid <= 16) a.counters[tid] = 0;   // work-claim counters
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int head_dim) {
+  plan_units<T>(a, head_dim, [&](int s) { return row_len(a, s); });
+}
+
+// ------------------------------------------------------------------------------ fused step prologue
+// The first kernel of a fused decode step: the device append, the scatter of the new tokens and the
+// plan, in one launch.  Workgroup 0 appends each row's new token (its block into the row's table,
+// the length up by one) and then plans over the lengths it has just written: each of its threads
+// appends and later reads back the same rows, so its own ordinary loads see its own stores.  The
+// other workgroups scatter the new tokens' keys and values, 256 key vectors per workgroup and four
+// threads per vector, after staging their tokens' slots in LDS (the slot mapping may live in pinned
+// host memory, so each slot is read once per workgroup that needs it).  The scatter and the append touch disjoint memory
+// and the plan reads only lengths, so the parts need no ordering between workgroups.
+template <typename T, bool FP8>
+__global__ __launch_bounds__(1024) void step_prologue_kernel(DecodeArgs a, ScatterArgs sc, StepArgs st,
+                                                             int head_dim) {
+  if (blockIdx.x == 0) {
+    const int S = a.num_seqs;
+    const int per = (S + 1023) / 1024;
+    const int lo = min(S, static_cast<int>(threadIdx.x) * per);
+    const int hi = min(S, lo + per);
+    for (int s = lo; s < hi; ++s) append_row(st.slots[s], st.block_tables, a.bt_stride, st.seq_lens, a.block_size, s);
+    plan_units<T>(a, head_dim, [&](int s) {
+      const int L = st.seq_lens[s];
+      return L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    });
+    return;
+  }
+  constexpr int C_ELEM = FP8 ? 16 : 16 / static_cast<int>(sizeof(T));   // elements per key vector
+  constexpr int kItems = 1024 / 4;           // key vectors per workgroup, four threads each
+  constexpr int kMaxTok = kItems / 4 + 2;    // 4 or more vectors per token (head_dim >= 64)
+  __shared__ int64_t slot_lds[kMaxTok];
+  const int C = sc.head_dim / C_ELEM;
+  const int64_t per_token = static_cast<int64_t>(sc.n_kv_heads) * C;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x - 1) * kItems;   // this workgroup's first vector
+  const int64_t total = per_token * sc.num_tokens;
+  const int t_first = static_cast<int>(i0 / per_token);
+  const int t_end = static_cast<int>(min(total - 1, i0 + kItems - 1) / per_token) + 1;   // past the last token
+  if (static_cast<int>(threadIdx.x) < min(t_end - t_first, kMaxTok))
+    slot_lds[threadIdx.x] = st.slots[t_first + threadIdx.x];
+  __syncthreads();
+  const int64_t item = i0 + (threadIdx.x >> 2);
+  if (item >= total) return;
+  const int sub = threadIdx.x & 3;
+  const int t = static_cast<int>(item / per_token);
+  const int rem = static_cast<int>(item - static_cast<int64_t>(t) * per_token);
+  const int h = rem / C;
+  const int c = rem - h * C;
+  if (t - t_first >= kMaxTok) return;   // (the host admits head_dim >= 64 only)
+  const int64_t slot = slot_lds[t - t_first];
+  if constexpr (FP8) {
+    scatter_quarter_fp8<T>(sc, t, h, c, sub, slot, st.k_scale, st.v_scale);
+  } else {
+    using E = typename std::conditional<sizeof(T) == 4, uint32_t, uint16_t>::type;
+    scatter_quarter<E>(sc, t, h, c, sub, slot);
+  }
 }
 
 // ------------------------------------------------------------------------------ tile pipeline
@@ -1135,6 +1197,27 @@ hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipS
   if (dtype == PKV_F32) decode_plan_kernel<float><<<1, 1024, 0, st>>>(a, head_dim);
   else if (dtype == PKV_F16) decode_plan_kernel<_Float16><<<1, 1024, 0, st>>>(a, head_dim);
   else decode_plan_kernel<__bf16><<<1, 1024, 0, st>>>(a, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_prologue(const DecodeArgs& a, const ScatterArgs& sc, const StepArgs& sa, int dtype,
+                                bool kv_fp8, int head_dim, hipStream_t st) {
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;   // the LDS slot stage assumes it
+  const int elem = kv_fp8 ? 16 : (dtype == PKV_F32 ? 4 : 8);             // elements per 16-byte key vector
+  const int64_t vectors = static_cast<int64_t>(sc.num_tokens) * sc.n_kv_heads * (sc.head_dim / elem);
+  const int64_t blocks = 1 + (vectors + 255) / 256;                     // 256 vectors per scatter workgroup
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grd(static_cast<unsigned>(blocks)), blk(1024);
+  if (dtype == PKV_F32) {
+    if (kv_fp8) return hipErrorInvalidValue;   // a quantised cache takes 16-bit rows and queries
+    step_prologue_kernel<float, false><<<grd, blk, 0, st>>>(a, sc, sa, head_dim);
+  } else if (dtype == PKV_F16) {
+    if (kv_fp8) step_prologue_kernel<_Float16, true><<<grd, blk, 0, st>>>(a, sc, sa, head_dim);
+    else step_prologue_kernel<_Float16, false><<<grd, blk, 0, st>>>(a, sc, sa, head_dim);
+  } else {
+    if (kv_fp8) step_prologue_kernel<__bf16, true><<<grd, blk, 0, st>>>(a, sc, sa, head_dim);
+    else step_prologue_kernel<__bf16, false><<<grd, blk, 0, st>>>(a, sc, sa, head_dim);
+  }
   return hipGetLastError();
 }
 

@@ -57,6 +57,15 @@ struct DecodeArgs {
   int32_t flat_bps;      // > 0: flat spans of this many blocks, block_tables holds one span per row
 };
 
+// The fused decode step's own arguments (beyond the scatter's and the decode's).
+struct StepArgs {
+  const int64_t* slots;   // one slot per batch row, at an address the kernel can read
+  int32_t* block_tables;  // the decode's tables and lengths, which the step's append updates
+  int32_t* seq_lens;
+  float k_scale;          // FP8 pools: the scatter stores codes of x / scale
+  float v_scale;
+};
+
 // Workspace carve-up shared by the size query and the launcher.
 struct WorkspaceLayout {
   size_t counters_off, units_off, m_off, l_off, acc_off, total;
@@ -81,6 +90,10 @@ hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, in
                                int32_t stride, int32_t* seq_lens, int32_t block_size,
                                hipStream_t stream);
 hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// The fused step's first kernel: append, scatter (sc.num_tokens == a.num_seqs tokens, rows of
+// dtype; kv_fp8: quantised pools) and plan.  head_dim must be 64 or 128.
+hipError_t launch_step_prologue(const DecodeArgs& a, const ScatterArgs& sc, const StepArgs& st, int dtype,
+                                bool kv_fp8, int head_dim, hipStream_t stream);
 // dtype: the type of q and of the results; kv_fp8: the pools hold FP8 E4M3 codes (else dtype)
 // path: 0 = vector, 1 = MFMA
 // nt: stream the key/value tiles with the non-temporal hint (otherwise ordinary cached loads)

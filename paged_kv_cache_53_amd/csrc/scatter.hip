@@ -3,121 +3,50 @@
 // reshape_and_cache writes every new token's key and value rows into the
 // physical slot the block manager gave it ("PagedAttention -- Math + Memory
 // Model", section "PagedAttention: blocks and the block table"); it copies
-// bits, never converts.  One thread moves one 16-byte vector of a key row
-// (X elements) and the X matching value elements:
-//   key:   one 16-byte store to (blk, h, c, off, 0..X-1)   -- coalesced along c
-//   value: X scalar stores to (blk, h, c*X + e, off)       -- the value pool keeps
-//          tokens contiguous per head dimension for the decode kernel's PV reads
-// reshape_and_cache_fp8 is the same scatter into a quantised cache: each
-// element x is stored as the FP8 E4M3 code of x / scale (fp32 division,
-// nearest code, ties to even, saturating at +-448, NaN to 0x7F), 16 codes per
-// 16-byte key vector.
+// bits, never converts.  reshape_and_cache_fp8 is the same scatter into a
+// quantised cache (codes of x / scale).  Four threads move one 16-byte key
+// vector and the matching value elements; the per-thread bodies are shared
+// with the fused decode-step prologue (scatter_body.h).
 // append_slots records, per batch row, the block of the new token's slot in
 // the row's block table and bumps the row's length.  copy_blocks makes the
 // private copies of shared blocks that copy-on-write appends ask for.
 #include <algorithm>
 
-#include "pkv_internal.h"
+#include "scatter_body.h"
 
 namespace pkv {
 namespace {
 
+// Thread gid -> (token t, head h, vector c, quarter sub) of a scatter with C vectors per head row.
+struct ScatterItem {
+  int t, h, c, sub;
+};
+__device__ inline bool scatter_item(const ScatterArgs& a, int C, ScatterItem& it) {
+  const int64_t per_token = static_cast<int64_t>(a.n_kv_heads) * C;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= 4 * per_token * a.num_tokens) return false;
+  const int64_t item = gid >> 2;
+  it.sub = static_cast<int>(gid & 3);
+  it.t = static_cast<int>(item / per_token);
+  const int rem = static_cast<int>(item - static_cast<int64_t>(it.t) * per_token);
+  it.h = rem / C;
+  it.c = rem - it.h * C;
+  return true;
+}
+
 template <typename E>  // E: uint32_t (fp32) or uint16_t (fp16/bf16) -- raw bits
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ScatterArgs a) {
-  constexpr int X = 16 / sizeof(E);
-  const int C = a.head_dim / X;                       // 16-byte vectors per row
-  const int64_t per_token = static_cast<int64_t>(a.n_kv_heads) * C;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= per_token * a.num_tokens) return;
-  const int t = static_cast<int>(gid / per_token);
-  const int rem = static_cast<int>(gid - static_cast<int64_t>(t) * per_token);
-  const int h = rem / C;
-  const int c = rem - h * C;
-  const int64_t slot = a.slot_mapping[t];
-  const int64_t cap = static_cast<int64_t>(a.num_blocks) * a.block_size;
-  if (slot < 0 || slot >= cap) return;
-  const int64_t blk = slot / a.block_size;
-  const int off = static_cast<int>(slot - blk * a.block_size);
-  const int64_t head_chunk = static_cast<int64_t>(a.head_dim) * a.block_size;  // elements
-  const int64_t base = (blk * a.n_kv_heads + h) * head_chunk;
-
-  const E* ksrc = static_cast<const E*>(a.k) + t * a.k_stride + static_cast<int64_t>(h) * a.head_dim + c * X;
-  const E* vsrc = static_cast<const E*>(a.v) + t * a.v_stride + static_cast<int64_t>(h) * a.head_dim + c * X;
-  const uint4 kv = *reinterpret_cast<const uint4*>(ksrc);
-  const uint4 vv = *reinterpret_cast<const uint4*>(vsrc);
-
-  E* kdst = static_cast<E*>(a.k_pool) + base + (static_cast<int64_t>(c) * a.block_size + off) * X;
-  *reinterpret_cast<uint4*>(kdst) = kv;
-
-  E vals[X];
-  __builtin_memcpy(vals, &vv, 16);
-  E* vdst = static_cast<E*>(a.v_pool) + base + static_cast<int64_t>(c) * X * a.block_size + off;
-#pragma unroll
-  for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * a.block_size] = vals[e];
+  ScatterItem it;
+  if (!scatter_item(a, a.head_dim / (16 / static_cast<int>(sizeof(E))), it)) return;
+  scatter_quarter<E>(a, it.t, it.h, it.c, it.sub, a.slot_mapping[it.t]);
 }
 
-// FP8 E4M3 code of x: sign, 4 exponent bits (bias 7), 3 mantissa bits; no infinities, S.1111.111
-// is NaN, so the largest finite magnitude is 448.  Nearest code with ties to the even mantissa,
-// magnitudes of 448 and above saturate to 448, NaN becomes 0x7F.
-__device__ inline uint32_t e4m3_code(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;                 // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (and infinities)
-  if (a >= 0x3C800000u) {                            // |x| >= 2^-6: normal codes
-    // keep 3 of the 23 mantissa bits, rounding to nearest even; a carry moves into the exponent.
-    // Then rebias the exponent from 127 to 7: code = (e - 120) << 3 | m = (a' >> 20) - (120 << 3).
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));
-  }
-  // below 2^-6 the codes are the multiples of 2^-9 (code m = m * 2^-9, m <= 8 reaches the smallest
-  // normal); |x| * 512 is exact and rintf rounds to nearest even
-  return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
-}
-
-template <typename S> __device__ inline float src_f32(S x) { return static_cast<float>(x); }
-
-// One thread: one 16-element key vector of one (token, head) and the 16 matching value elements.
+// Four threads per 16-element key vector of one (token, head) and the 16 matching value elements.
 template <typename S>  // source element type: float, _Float16 or __bf16
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ScatterArgs a, float k_scale, float v_scale) {
-  constexpr int X = 16;
-  const int C = a.head_dim / X;
-  const int64_t per_token = static_cast<int64_t>(a.n_kv_heads) * C;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= per_token * a.num_tokens) return;
-  const int t = static_cast<int>(gid / per_token);
-  const int rem = static_cast<int>(gid - static_cast<int64_t>(t) * per_token);
-  const int h = rem / C;
-  const int c = rem - h * C;
-  const int64_t slot = a.slot_mapping[t];
-  const int64_t cap = static_cast<int64_t>(a.num_blocks) * a.block_size;
-  if (slot < 0 || slot >= cap) return;
-  const int64_t blk = slot / a.block_size;
-  const int off = static_cast<int>(slot - blk * a.block_size);
-  const int64_t base = (blk * a.n_kv_heads + h) * static_cast<int64_t>(a.head_dim) * a.block_size;  // bytes
-
-  constexpr int NV = X * sizeof(S) / 16;   // 16-byte source vectors per 16 elements
-  const S* ksrc = static_cast<const S*>(a.k) + t * a.k_stride + static_cast<int64_t>(h) * a.head_dim + c * X;
-  const S* vsrc = static_cast<const S*>(a.v) + t * a.v_stride + static_cast<int64_t>(h) * a.head_dim + c * X;
-  uint4 kraw[NV], vraw[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    kraw[i] = reinterpret_cast<const uint4*>(ksrc)[i];
-    vraw[i] = reinterpret_cast<const uint4*>(vsrc)[i];
-  }
-  S kx[X], vx[X];
-  __builtin_memcpy(kx, kraw, sizeof(kx));
-  __builtin_memcpy(vx, vraw, sizeof(vx));
-  uint32_t kw[4] = {0u, 0u, 0u, 0u};
-  uint8_t* kdst = static_cast<uint8_t*>(a.k_pool) + base + (static_cast<int64_t>(c) * a.block_size + off) * X;
-  uint8_t* vdst = static_cast<uint8_t*>(a.v_pool) + base + static_cast<int64_t>(c) * X * a.block_size + off;
-#pragma unroll
-  for (int e = 0; e < X; ++e) {
-    kw[e >> 2] |= e4m3_code(src_f32(kx[e]) / k_scale) << (8 * (e & 3));
-    vdst[static_cast<int64_t>(e) * a.block_size] = static_cast<uint8_t>(e4m3_code(src_f32(vx[e]) / v_scale));
-  }
-  *reinterpret_cast<uint4*>(kdst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  ScatterItem it;
+  if (!scatter_item(a, a.head_dim / 16, it)) return;
+  scatter_quarter_fp8<S>(a, it.t, it.h, it.c, it.sub, a.slot_mapping[it.t], k_scale, v_scale);
 }
 
 __global__ __launch_bounds__(256) void append_slots_kernel(const int64_t* __restrict__ slot_mapping,
@@ -126,13 +55,7 @@ __global__ __launch_bounds__(256) void append_slots_kernel(const int64_t* __rest
                                                            int32_t block_size) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= num_seqs) return;
-  const int64_t slot = slot_mapping[i];
-  const int32_t p = seq_lens[i];
-  if (slot < 0 || p < 0) return;
-  const int32_t bi = p / block_size;
-  if (bi >= stride) return;
-  block_tables[static_cast<int64_t>(i) * stride + bi] = static_cast<int32_t>(slot / block_size);
-  seq_lens[i] = p + 1;
+  append_row(slot_mapping[i], block_tables, stride, seq_lens, block_size, i);
 }
 
 // Block copies between two block arrays (the same pool for copy-on-write; a device pool and host
@@ -177,7 +100,7 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, 
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t stream) {
   const int esz = dtype == PKV_F32 ? 4 : 2;
-  const int64_t work = static_cast<int64_t>(a.num_tokens) * a.n_kv_heads * (a.head_dim * esz / 16);
+  const int64_t work = 4 * static_cast<int64_t>(a.num_tokens) * a.n_kv_heads * (a.head_dim * esz / 16);  // threads
   if (work == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (work + threads - 1) / threads;
@@ -191,7 +114,7 @@ hipError_t launch_reshape_and_cache(const ScatterArgs& a, int dtype, hipStream_t
 
 hipError_t launch_reshape_and_cache_fp8(const ScatterArgs& a, int src_dtype, float k_scale, float v_scale,
                                         hipStream_t stream) {
-  const int64_t work = static_cast<int64_t>(a.num_tokens) * a.n_kv_heads * (a.head_dim / 16);
+  const int64_t work = 4 * static_cast<int64_t>(a.num_tokens) * a.n_kv_heads * (a.head_dim / 16);  // threads
   if (work == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (work + threads - 1) / threads;

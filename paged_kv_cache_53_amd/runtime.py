@@ -8,14 +8,17 @@ PagedKVCache   one layer's key/value pools on the device and the host block allo
                scales k_scale / v_scale (the scatter quantises, decode reads the scaled values).
 DecodeBatch    a fixed set of sequences decoded together: device block tables and lengths,
                a workspace, and ``step()`` -- one decode step of the whole hot path:
-                 1. host: the allocator appends one token to every sequence (C++, one call)
-                 2. the new slots go to the device through a pinned, double-buffered stage
-                 3. copy_blocks kernel, when an append hit a shared block (copy-on-write)
-                    append_slots kernel: new block ids into the device tables, lengths + 1
-                 4. reshape_and_cache kernel: the new tokens' K/V into their slots
-                 5. paged decode (plan, main, merge kernels)
+                 1. host: the allocator appends one token to every sequence (C++, one call),
+                    writing the new slots into a pinned, double-buffered stage
+                 2. copy_blocks kernel, when an append hit a shared block (copy-on-write)
+                 3. decode_step: a prologue kernel (append of the new block ids into the device
+                    tables and lengths + 1, the plan of the attention's work, and the scatter of
+                    the new tokens' K/V into their slots; the slots are read from the stage in
+                    place), then the attention and merge kernels
+               (``step(fused=False)`` copies the slots to the device and makes the separate
+               append_slots, reshape_and_cache and paged_attention_decode calls instead.)
                Host work for step i+1 overlaps the GPU work of step i; the host waits only
-               before reusing a staging buffer that a copy may still be reading.
+               before reusing a staging buffer that a step may still be reading.
 FlatKVCache    the flat-span alternative: one contiguous virtual span per sequence (SpanPool),
                physical memory mapped as the sequence grows, no block table.
 FlatDecodeBatch  one decode step over flat spans: span backing grown on the host when a token
@@ -30,7 +33,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (Allocator, SpanPool, append_slots, copy_blocks, key_pool_shape, paged_attention_decode,
+from . import (Allocator, SpanPool, append_slots, copy_blocks, decode_step, key_pool_shape, paged_attention_decode,
                paged_attention_decode_flat, reshape_and_cache, reshape_and_cache_spans, swap_blocks,
                value_pool_shape, workspace_size)
 
@@ -141,32 +144,61 @@ class DecodeBatch:
         self.host_lens = lens.astype(np.int64)
         self.workspace = torch.empty(max(256, workspace_size(self.S, n_q_heads, cache.head_dim, max_seq_len,
                                                                partition_size)), dtype=torch.uint8, device=dev)
-        self.slot_stage = [torch.empty(self.S, dtype=torch.int64, pin_memory=True) for _ in range(2)]
+        # A ring of pinned slot stages, and a completion event every STAGE_EVENT_EVERY steps: an event
+        # record costs the stream a few microseconds, so one per step would be a measurable share of
+        # a step.  Before a stage is rewritten, the step that last read it must have finished.
+        self.slot_stage = [torch.empty(self.S, dtype=torch.int64, pin_memory=True) for _ in range(self.STAGES)]
         self.slot_stage_np = [t.numpy() for t in self.slot_stage]
-        self.stage_done = [None, None]
+        self.step_events = {}     # step index -> event recorded after that step
         self.slot_dev = torch.empty(self.S, dtype=torch.int64, device=dev)
         self.steps = 0
 
-    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor) -> None:
-        """One decode step for every row: append the new token, write its K/V, attend over all tokens."""
+    STAGES = 8
+    STAGE_EVENT_EVERY = 4
+
+    def _stage_for(self, n: int) -> int:
+        """The stage of step n, once the step that last read it (n - STAGES) has finished."""
+        m = n - self.STAGES
+        if m >= 0:
+            e = m + (-(m + 1)) % self.STAGE_EVENT_EVERY     # the first event step >= m (several n share it)
+            ev = self.step_events.get(e)
+            if ev is None:
+                torch.cuda.current_stream().synchronize()    # not expected: fall back to a full wait
+            else:
+                ev.synchronize()
+            for k in [k for k in self.step_events if k < e]:
+                del self.step_events[k]
+        return n % self.STAGES
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor,
+             fused: bool = True) -> None:
+        """One decode step for every row: append the new token, write its K/V, attend over all tokens.
+
+        fused: one decode_step call, which reads the slots from their pinned staging buffer in place;
+        otherwise the slots are copied to the device and append_slots, reshape_and_cache and
+        paged_attention_decode run as separate calls.  The results are the same."""
         if int(self.host_lens.max(initial=0)) + 1 > self.max_seq_len:
             raise ValueError("decode step would exceed max_seq_len")
-        i = self.steps & 1
-        if self.stage_done[i] is not None:
-            self.stage_done[i].synchronize()          # the copy that last read this stage is done
+        i = self._stage_for(self.steps)
         _, pairs = self.cache.allocator.alloc_batch(self.seq_ids, 1, slots_out=self.slot_stage_np[i])
         self.host_lens += 1
-        self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self.stage_done[i] = ev
         c = self.cache
         c.apply_copies(pairs)   # a forked row writing into a shared block gets its private copy first
-        append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
-        reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool, **c.scales)
-        paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
-                               self.max_seq_len, self.partition_size, workspace=self.workspace,
-                               shared_kv=c.has_shared_blocks(), **c.scales)
+        if fused:
+            decode_step(out, q, k_new, v_new, self.slot_stage[i], c.k_pool, c.v_pool, self.tables, self.seq_lens,
+                        self.scale, self.max_seq_len, self.partition_size, workspace=self.workspace,
+                        shared_kv=c.has_shared_blocks(), **c.scales)
+        else:
+            self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
+            append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
+            reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool, **c.scales)
+            paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
+                                   self.max_seq_len, self.partition_size, workspace=self.workspace,
+                                   shared_kv=c.has_shared_blocks(), **c.scales)
+        if (self.steps + 1) % self.STAGE_EVENT_EVERY == 0:
+            ev = torch.cuda.Event()
+            ev.record()
+            self.step_events[self.steps] = ev
         self.steps += 1
 
     def refresh(self) -> None:

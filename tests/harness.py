@@ -25,7 +25,10 @@ class GpuState:
     """Pools, tables, lengths and q built by the library's own allocator and scatter kernel."""
 
     def __init__(self, w: wl.Workload, poison: bool = True, table_pad: int = 0x3FFFFFF0,
-                 device: str = "cuda", extra_table_cols: int = 2):
+                 device: str = "cuda", extra_table_cols: int = 2, step: bool = True):
+        """step=False stops before the decode step's device work: the tables and lengths hold the
+        prompts, and the step's slots (step_slots, int64 numpy) and new rows (kn, vn) are left
+        for the caller to apply."""
         import paged_kv_cache_53_amd as pkv
         self.w, self.pkv = w, pkv
         dt = TORCH_DTYPE[w.dtype]
@@ -65,15 +68,24 @@ class GpuState:
                 self.alloc.fork(op["parent"], op["child"], op["n"])
             else:
                 self.alloc.free(op["seq"])
-        # the decode step: one new token per row, scattered before attention
-        slots, pairs = self.alloc.alloc_batch(w.batch.tolist(), 1)
-        assert not pairs
-        self.new_slots = torch.from_numpy(slots.copy()).to(device)
-        kn, vn = wl.new_token_kv(w, device=device)
-        pkv.reshape_and_cache(kn, vn, self.new_slots, self.k_pool, self.v_pool, **self.scales)
         self.stride = int(math.ceil(max(w.max_seq_len, 1) / w.block_size)) + extra_table_cols
-        tables, lens = self.alloc.fill_block_tables(w.batch.tolist(), self.stride, pad=table_pad)
-        assert np.array_equal(lens, w.seq_lens)
+        kn, vn = wl.new_token_kv(w, device=device)
+        if step:
+            # the decode step: one new token per row, scattered before attention
+            slots, pairs = self.alloc.alloc_batch(w.batch.tolist(), 1)
+            assert not pairs
+            self.new_slots = torch.from_numpy(slots.copy()).to(device)
+            pkv.reshape_and_cache(kn, vn, self.new_slots, self.k_pool, self.v_pool, **self.scales)
+            tables, lens = self.alloc.fill_block_tables(w.batch.tolist(), self.stride, pad=table_pad)
+            assert np.array_equal(lens, w.seq_lens)
+        else:
+            self.alloc.alloc_batch(w.batch.tolist(), 0)     # rows with no prompt exist, empty
+            tables, lens = self.alloc.fill_block_tables(w.batch.tolist(), self.stride, pad=table_pad)
+            assert np.array_equal(lens, w.seq_lens - 1)
+            slots, pairs = self.alloc.alloc_batch(w.batch.tolist(), 1)
+            assert not pairs
+            self.step_slots = slots.copy()
+            self.kn, self.vn = kn, vn
         self.tables_host = tables
         self.tables = torch.from_numpy(tables).to(device)
         self.seq_lens = torch.from_numpy(lens.copy()).to(device)

@@ -210,3 +210,64 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(_lib.LibraryNotBuilt):
         _lib.load()
+
+
+def _step_args(**kw):
+    F16 = pkv.PKV_F16
+    a = dict(k=16, v=16, k_token_stride=0, v_token_stride=0, slot_mapping=16, k_pool=16, v_pool=16, num_blocks=100,
+             kv_fp8=0, k_scale=1.0, v_scale=1.0, block_tables=16, seq_lens=16, block_table_stride=8, num_seqs=2,
+             n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16, out=16, out_dtype=F16, dtype=F16, q=16,
+             scale=0.1, max_seq_len=128, partition_size=512, flags=0, workspace=256, workspace_bytes=1 << 30)
+    a.update(kw)
+    return _lib.pkv_decode_step_args(**a)
+
+
+def test_decode_step_rejects_bad_arguments_before_any_hip_call():
+    lib = pkv.lib()
+    step = lambda **kw: lib.pkv_decode_step(_step_args(**kw), None)   # noqa: E731
+    BF16, F32 = pkv.PKV_BF16, pkv.PKV_F32
+    assert lib.pkv_decode_step(None, None) == pkv.PKV_ERR_INVALID
+    assert step(num_seqs=0, k=None, v=None, slot_mapping=None) == pkv.PKV_OK      # empty: no launch
+    assert step(k=None) == pkv.PKV_ERR_INVALID
+    assert step(v=24) == pkv.PKV_ERR_INVALID                                       # misaligned row
+    assert step(slot_mapping=None) == pkv.PKV_ERR_INVALID
+    assert step(slot_mapping=20) == pkv.PKV_ERR_INVALID                            # misaligned slots
+    assert step(k_token_stride=100) == pkv.PKV_ERR_INVALID                         # stride < row
+    assert step(block_table_stride=7) == pkv.PKV_ERR_INVALID                       # 128 tokens need 8
+    assert step(kv_fp8=2) == pkv.PKV_ERR_INVALID
+    assert step(kv_fp8=1, k_scale=0.0) == pkv.PKV_ERR_INVALID                      # scales positive
+    assert step(kv_fp8=1, v_scale=float("inf")) == pkv.PKV_ERR_INVALID             # and finite
+    assert step(kv_fp8=1, dtype=F32, out_dtype=F32, n_q_heads=4) == pkv.PKV_ERR_UNSUPPORTED   # fp8: 16-bit q
+    assert step(dtype=pkv.PKV_FP8_E4M3) == pkv.PKV_ERR_INVALID                    # rows are never codes
+    assert step(head_dim=100) == pkv.PKV_ERR_INVALID                               # 8 elements per vector
+    assert step(head_dim=96) == pkv.PKV_ERR_UNSUPPORTED                            # the decode's dims
+    assert step(out_dtype=BF16) == pkv.PKV_ERR_INVALID
+    assert step(scale=float("inf")) == pkv.PKV_ERR_INVALID
+    assert step(flags=4) == pkv.PKV_ERR_INVALID
+    assert step(workspace_bytes=1024) == pkv.PKV_ERR_INVALID
+
+
+def test_decode_step_args_layout_matches_the_header():
+    """The ctypes structure has the C struct's size and field offsets (compiled with the host C
+    compiler from include/pkv.h)."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in _lib.pkv_decode_step_args._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"pkv.h\"\nint main(void) {\n"
+    src += '  printf("%zu\\n", sizeof(pkv_decode_step_args));\n'
+    for f in fields:
+        src += f'  printf("%zu\\n", offsetof(pkv_decode_step_args, {f}));\n'
+    src += "  return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()]
+    import ctypes
+    want = [ctypes.sizeof(_lib.pkv_decode_step_args)] + [getattr(_lib.pkv_decode_step_args, f).offset
+                                                          for f in fields]
+    assert got == want
