@@ -2,10 +2,13 @@
 """Paged decode attention throughput on one MI355X.
 
 A step is one decode step of the whole hot path for every sequence of the
-batch: the host allocator appends one token per sequence, the new slots are
-staged to the device, the append kernel extends the device block tables,
-the scatter kernel writes the new tokens' K/V, and paged decode attention
-(plan, main, merge kernels) reads every sequence's K/V through its table.
+batch: the host allocator appends one token per sequence into a pinned slot
+stage, then one fused decode step runs on the device: a prologue kernel
+extends the device block tables and lengths, plans the attention's work and
+writes the new tokens' K/V into their slots (reading the slots from the stage
+in place), and paged decode attention (main and merge kernels) reads every
+sequence's K/V through its table.  --unfused makes the separate calls instead
+(slot copy, append, scatter, plan, main, merge), with the same results.
 The default workload is the Llama-3-70B-class layer: 256 sequences,
 log-normal lengths (median 3000, clipped to [16, 32768]), 64 q / 8 KV heads,
 head_dim 128, bf16 KV, 16-token blocks scattered through the pool, 2048-token
