@@ -193,3 +193,38 @@ def test_runtime_steps_fused_equal_unfused_with_forks(kv):
     for x, y in zip(pools[True], pools[False]):
         assert torch.equal(_bits(x), _bits(y))
     assert torch.isfinite(outs[True][-1].float()).all()
+
+
+def _sample_rows(w, n=6):
+    """The longest and shortest rows plus a seeded sample (the oracle computes them one by one)."""
+    order = np.argsort(w.seq_lens)
+    rng = np.random.default_rng(w.seed + 100)
+    rows = {int(order[0]), int(order[-1])} | {int(r) for r in rng.choice(w.num_seqs, size=n - 2, replace=False)}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("kv", ["native", "fp8"])
+def test_step_full_size_llama70b_batch(kv):
+    """The bench's workload and launch (256 rows, 1.2 M tokens, partitions of 2048): the fused step
+    leaves the same bits as the separate calls, and sampled rows match the oracle."""
+    w = wl.build(3)
+    if kv == "fp8":
+        w = wl.quantised(w)
+    log(f"full config 3, {kv} cache: {w.describe()}")
+    a, b = _two_states(w)
+    out_a = torch.empty(w.num_seqs, w.n_q_heads, w.head_dim, dtype=TORCH_DTYPE[w.dtype], device="cuda")
+    out_b = torch.empty_like(out_a)
+    _run_fused(a, torch.from_numpy(a.step_slots).pin_memory(), out_a)
+    _run_separate(b, torch.from_numpy(b.step_slots).to("cuda"), out_b)
+    torch.cuda.synchronize()
+    _assert_same_state(a, b, out_a, out_b)
+    del b
+    torch.cuda.empty_cache()
+    rows = _sample_rows(w)
+    from harness import oracle_rows
+    ref = oracle_rows(w, rows)
+    err = max_abs_err(out_a, ref, rows=rows)
+    log(f"  rows {rows}: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype], err
+    del a
+    torch.cuda.empty_cache()
