@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--block-size", type=int, default=None)
     p.add_argument("--placement", default="random", choices=["random", "identity"])
     p.add_argument("--partition-size", type=int, default=None, help="default: the workload's own")
+    p.add_argument("--seed", type=int, default=None,
+                   help="another draw of the workload's distributions (default: the config's own seed)")
     p.add_argument("--copied-prefix", action="store_true", help="config 4: private prefix copies")
     p.add_argument("--kv-dtype", default="native", choices=["native", "fp8"],
                    help="fp8: the cache stores FP8 E4M3 codes (per-tensor scales)")
@@ -408,7 +410,7 @@ def step_description(args):
 def make_workload(args):
     import workloads as wl
     w = wl.build(args.config, block_size=args.block_size, placement=args.placement,
-                 copied_prefix=args.copied_prefix, partition_size=args.partition_size)
+                 copied_prefix=args.copied_prefix, partition_size=args.partition_size, seed=args.seed)
     return wl.quantised(w) if args.kv_dtype == "fp8" else w
 
 

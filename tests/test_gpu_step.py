@@ -205,7 +205,7 @@ def _sample_rows(w, n=6):
 
 @pytest.mark.parametrize("kv", ["native", "fp8"])
 def test_step_full_size_llama70b_batch(kv):
-    """The bench's workload and launch (256 rows, 1.2 M tokens, partitions of 2048): the fused step
+    """The bench's workload and launch (256 rows, 1.2 M tokens, partitions of 3072): the fused step
     leaves the same bits as the separate calls, and sampled rows match the oracle."""
     w = wl.build(3)
     if kv == "fp8":
