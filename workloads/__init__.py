@@ -216,7 +216,9 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
 
     if config_id == 4:
         # Agent swarm: 20 sequences share one 4000-token prompt (250 blocks), then private
-        # suffixes U[0, 12000]; 32 q / 8 kv heads, fp16, B=16.
+        # suffixes U[0, 12000]; 32 q / 8 kv heads, fp16, B=16.  768-token partitions (a launch
+        # choice): over two draws (seeds 3 and 9) a decode call took 0.140 / 0.134 / 0.148 ms and
+        # 0.183 / 0.177 / 0.174 ms at 512 / 768 / 1024 on MI355X.
         bsz = block_size or 16
         if small:
             n_children, prefix, suffixes = 5, 400, rng_len.integers(0, 600, size=5, endpoint=True)
@@ -245,7 +247,7 @@ def build(config_id: int, *, small: bool = False, block_size: Optional[int] = No
                         head_dim=128, block_size=bsz, dtype="f16", num_blocks=n_blocks,
                         free_order=_free_order(rng_place, n_blocks, placement),
                         prompt_ops=ops, batch=np.arange(n_children, dtype=np.int64),
-                        seq_lens=lens, segments=segs, partition_size=partition_size or 512,
+                        seq_lens=lens, segments=segs, partition_size=partition_size or 768,
                         placement=placement,
                         variant=variant + ("-copied" if copied_prefix else "-shared"))
 
