@@ -465,10 +465,11 @@ struct Tile16 {
 
 // Register-resident tile of 32 tokens of an FP8 cache: the same bytes per tile and the same
 // load widths as a 16-token tile of 16-bit KV.  The QK product runs as two 16-row MFMA blocks;
-// row r of block b is token 8(r/4) + 4b + r%4, so the two accumulators give lane (head, g) the
-// scores of tokens 8g..8g+7 -- exactly the B operand of one 32-deep PV MFMA, whose A operand is
-// then 8 consecutive codes of one value dim (one 8-byte load).
-//   kf[b][ks]: lane (row r16, g) holds 16-code key vector 4ks+g of token 8(r16/4) + 4b + r16%4
+// row r of block b is token 16b + r, so every key load reads whole 128-byte lines, and the two
+// accumulators give lane (head, g) the scores of tokens 4g..4g+3 and 16+4g..16+4g+3.  Two row
+// swaps move the probabilities to tokens 8g..8g+7 (compute32), the B operand of one 32-deep PV
+// MFMA whose A operand is then 8 consecutive codes of one value dim (one 8-byte load).
+//   kf[b][ks]: lane (row r16, g) holds 16-code key vector 4ks+g of token 16b + r16
 //   vf[dt]:    lane (dim 16dt + r16, g) holds the codes of tokens 8g..8g+7
 template <int D>
 struct Tile32F8 {
@@ -495,20 +496,21 @@ struct Tile32F8 {
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) id[j] = min(max(id[j], 0), a.num_blocks - 1);
-    // key rows: token 8(r16/4) + 4b + r16%4 lies in block (r16/4) / TPB of the tile
-    const int jk = (r16 >> 2) / TPB;
-    int bk = id[0];
-#pragma unroll
-    for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
-    // The two row blocks read the two 64-byte halves of every 128-byte key line (tokens 8i..8i+3 and
-    // 8i+4..8i+7), so key lines stay cacheable: with the non-temporal hint the second half came from
-    // HBM again (4 % more fetch; 465 us instead of 449 us on the Llama-70B-class batch).
+    // key rows: row r16 of block b is token 16b + r16.  Each load reads whole key lines (a block of
+    // 16 rows holds 16 consecutive tokens of one 16-code vector), so it takes the stream's policy.
+    // The previous row order (token 8(r/4) + 4b + r%4, which left the scores in the PV layout
+    // directly) read every line in two 64-byte halves from two loads: 450 against 437 us on the
+    // Llama-70B-class batch, where it had to keep key lines cacheable.
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int tok = (8 * (r16 >> 2) + 4 * b + (r16 & 3)) & (Bsz - 1);
-      const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + tok) * 16;
+      const int tt = 16 * b + r16;
+      const int jk = tt / Bsz;
+      int bk = id[0];
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) vload<E, false>(kf[b][ks], kb + ks * 4 * Bsz * 16);
+      for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
+      const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + (tt & (Bsz - 1))) * 16;
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[b][ks], kb + ks * 4 * Bsz * 16);
     }
     // value dims: tokens 8g..8g+7 lie in block g / TPB
     const int jv = g / TPB;
@@ -697,7 +699,9 @@ struct MfmaMath {
   }
   // 32 tokens of FP8 codes widened to T: two 16-row QK blocks per 32 dims, then one 32-deep
   // PV MFMA per 16 dims.  Lane (head r16, g) ends the QK product with the scores of tokens
-  // 8g..8g+7 (block 0 rows 4g..4g+3 are tokens 8g..8g+3, block 1 rows are tokens 8g+4..8g+7).
+  // 4g..4g+3 (block 0) and 16+4g..16+4g+3 (block 1); the softmax works in that layout (its
+  // maxima and sums run over all four rows g), and two row swaps then hand the PV product the
+  // weights of tokens 8g..8g+7.
   __device__ void compute32(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     using V8 = typename Vec8<T>::type;
     const int g = threadIdx.x >> 4;
@@ -713,7 +717,7 @@ struct MfmaMath {
       s0 = mfma_16x16x32(a0, qv, s0);
       s1 = mfma_16x16x32(a1, qv, s1);
     }
-    float x[8];   // token 8g + i
+    float x[8];   // tokens 4g + i (i < 4) and 16 + 4g + i - 4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = s0[i] * scale_log2;
@@ -723,7 +727,7 @@ struct MfmaMath {
     if (partial) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (t0 + 8 * g + i >= ntok) x[i] = -INFINITY;
+        if (t0 + (i < 4 ? 4 * g + i : 12 + 4 * g + i) >= ntok) x[i] = -INFINITY;
     }
     float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mt = max_x32(max_x16(mt));
@@ -738,8 +742,26 @@ struct MfmaMath {
       psum += to_f32(pt[i]);
     }
     l_run = l_run * alpha + psum;
+    // From the QK layout (pw[0..1]: tokens 4g..4g+3, pw[2..3]: tokens 16+4g..16+4g+3) to the PV
+    // layout (tokens 8g..8g+7): the half swap gives rows g < 2 the first words of row g+2 as their
+    // second words and rows g >= 2 the second words of row g-2 as their first; the row swap then
+    // exchanges the second words of even rows with the first words of odd rows.
+    unsigned pw[4];
+    __builtin_memcpy(pw, pt, 16);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pw[w], pw[2 + w], false, false);
+      pw[w] = r[0];
+      pw[2 + w] = r[1];
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane16_swap(pw[w], pw[2 + w], false, false);
+      pw[w] = r[0];
+      pw[2 + w] = r[1];
+    }
     V8 pb;
-    __builtin_memcpy(&pb, pt, 16);
+    __builtin_memcpy(&pb, pw, 16);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       V8 va = widen8<T>(R.vf[dt][0], R.vf[dt][1]);
