@@ -161,8 +161,10 @@ def test_step_rejects_pageable_host_slots():
 
 @pytest.mark.parametrize("kv", ["native", "fp8"])
 def test_runtime_steps_fused_equal_unfused_with_forks(kv):
-    """Several runtime steps over forked rows (copy-on-write on the first append into a shared,
-    partly filled block): the fused and the separate-call steps give the same bits every step."""
+    """Twenty runtime steps over forked rows (copy-on-write on the first append into a shared,
+    partly filled block): the fused and the separate-call steps give the same bits every step.
+    Twenty steps cycle the batch's ring of slot stages more than twice, so stages are rewritten
+    after the step that read them has finished."""
     from paged_kv_cache_53_amd.runtime import DecodeBatch, PagedKVCache
     Hk, D, B, G = 2, 128, 16, 4
     outs, pools = {}, {}
@@ -178,7 +180,7 @@ def test_runtime_steps_fused_equal_unfused_with_forks(kv):
         cache.append(3, prompt[:20], prompt[:20] * 2)
         batch = DecodeBatch(cache, [0, 1, 2, 3], G * Hk, 128, partition_size=32)
         seq = []
-        for i in range(6):
+        for i in range(20):
             q = torch.randn(4, G * Hk, D, generator=g).to(torch.bfloat16).cuda()
             kn = torch.randn(4, Hk, D, generator=g).to(torch.bfloat16).cuda()
             vn = torch.randn(4, Hk, D, generator=g).to(torch.bfloat16).cuda()
