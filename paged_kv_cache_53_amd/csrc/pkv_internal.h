@@ -34,7 +34,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   // workspace views
-  int32_t* counters;     // [0] = number of (row, partition) units, [1] = next unit to hand out
+  int32_t* counters;     // [0] = number of (row, partition) units, [1] = units handed out after the
+                         // first gridDim.x, which the waves of the persistent grid start on
   int2* units;           // (row, partition) pairs, row-major, partitions ascending
   float* part_m;         // [S][Hq][max_parts]  running max of x*log2(e)
   float* part_l;         // [S][Hq][max_parts]  sum of weights
