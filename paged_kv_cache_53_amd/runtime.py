@@ -162,8 +162,8 @@ class DecodeBatch:
 
     def _keep_cached(self) -> bool:
         """Decode with cacheable loads: blocks shared between rows, or a small FP8 batch.  On MI355X
-        an FP8 opt13b-class batch (0.36 GB) took 99.7 us cacheable against 103 us streamed, the
-        Llama-70B-class one (2.5 GB) 474 against 437 us."""
+        an FP8 opt13b-class batch (0.36 GB) took 80.9 us cacheable against 82.9 us streamed, the
+        Llama-70B-class one (2.5 GB) 474 against 437 us; a bf16 opt13b-class batch 133 against 126 us."""
         c = self.cache
         if c.has_shared_blocks():
             return True
