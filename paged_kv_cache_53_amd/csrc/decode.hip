@@ -964,13 +964,21 @@ void decode_kernel(DecodeArgs a) {
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
   __shared__ u32x4 q_lds[2][Math::QH][NQ][64];   // q fragments: compute unit's and issue unit's
 
-  // Wave w starts on unit w, and the counter hands out the units after the grid's first ones:
-  // every wave claiming its first unit from the one counter at once serialised 2048 atomics and
-  // delayed the last waves' start (Llama-70B-class batch 789 -> 769 us, opt13b-class 146 -> 126 us,
-  // swarm 118 -> 88 us once the first claims went).  Units are ordered longest first, so the
-  // grid's first units are the ones the counter would have handed out first anyway.
+  // Each wave starts on one of the grid's first units, and the counter hands out the units after
+  // them: every wave claiming its first unit from the one counter at once serialised 2048 atomics
+  // and delayed the last waves' start (Llama-70B-class batch 789 -> 769 us, opt13b-class 146 ->
+  // 126 us, swarm 118 -> 88 us once the first claims went).  Units are ordered longest first, so
+  // the grid's first units are the ones the counter would have handed out first anyway.
+  // Which first unit: workgroups are dispatched to the 8 XCDs in turn, so wave w runs on XCD w % 8.
+  // Streamed (each block read by one row): XCD x starts on the x-th eighth of the units, every KV
+  // head of consecutive (row, partition) pairs, so a row's table lines and blocks stay with one XCD
+  // (1 % faster on the Llama-70B-class and opt13b-class batches).  Cacheable (blocks shared between
+  // rows): wave w starts on unit w, KV head w % 8, so XCD x reads head x of every row and keeps the
+  // shared blocks' lines of that head in its L2 (the other order made the swarm 14 % slower).
   int pending = 0;
-  const int first = blockIdx.x;
+  const int first = (NT && !(gridDim.x & 7))
+                        ? static_cast<int>((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                        : static_cast<int>(blockIdx.x);
   if (first >= total) return;
   Unit<KV> uc = open_unit<KV, FLAT>(a, first, chunk);   // compute cursor
   Unit<KV> ui = uc;                              // issue cursor
