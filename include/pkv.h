@@ -274,7 +274,8 @@ int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int 
  *   slot_mapping   int64 [num_seqs]: the slot of row s's new token (token s of k and v), as the
  *                  allocator gave it; a negative slot skips the row's scatter and append.  Device
  *                  memory or pinned host memory (hipHostMalloc): the prologue reads
- *                  host memory over the host link, once per token, so the step needs no copy.
+ *                  host memory over the host link (each slot once for the append and once per
+ *                  scatter workgroup that covers its token), so the step needs no copy.
  *                  It must not change until the prologue has run.  Pageable host memory:
  *                  PKV_ERR_INVALID.
  *   k, v           device rows, token s of each at s * k_token_stride (v_token_stride) elements of
