@@ -11,14 +11,19 @@ sequence's K/V through its table.  --unfused makes the separate calls instead
 (slot copy, append, scatter, plan, main, merge), with the same results.
 The default workload is the Llama-3-70B-class layer: 256 sequences,
 log-normal lengths (median 3000, clipped to [16, 32768]), 64 q / 8 KV heads,
-head_dim 128, bf16 KV, 16-token blocks scattered through the pool, 2048-token
+head_dim 128, bf16 KV, 16-token blocks scattered through the pool, 3072-token
 partitions.  All inputs are the seeded synthetic workload, resident in HBM
 before the timed region.
 
 Prints one JSON line: value = algorithmic KV-read GB/s over whole steps
 (K + V bytes of every valid token plus block-table bytes), with seqs/s, the
-decode kernel's roofline (HIP events on the kernel's stream), and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+decode kernel's roofline (HIP events on the kernel's stream), the decode
+kernel's per-launch median / p10 / p90 over separately collected launches
+after the timed region (--flush adds the same over launches that each follow
+a 1 GiB write, and over launches that each follow a 1 GiB read: either evicts
+L2 and the 256 MB Infinity Cache), the device,
+engine clock and ROCm version, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16]
                     [--placement random|identity] [--kv-dtype native|fp8] [--no-cpu-baseline] [--sweep]
@@ -70,6 +75,13 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--sweep", action="store_true", help="config-5 block-size x placement sweep (decode only)")
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
+    p.add_argument("--reps", type=int, default=20,
+                   help="separately collected launches for the decode kernel's median / p10 / p90")
+    p.add_argument("--load-policy", default="auto", choices=["auto", "streamed", "cached"],
+                   help="how decode reads the pools (auto: the runtime's rule)")
+    p.add_argument("--flush", action="store_true",
+                   help="also time --reps launches after a 1 GiB write and --reps after a 1 GiB read "
+                        "(each evicts L2 and MALL)")
     p.add_argument("--unfused", action="store_true",
                    help="paged steps as separate calls (slot copy, append_slots, scatter, decode) instead of "
                         "one decode_step")
@@ -142,14 +154,27 @@ def kv_bytes(w, lens, table=True):
 
 
 # ------------------------------------------------------------------------------------- GPU timing
-def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True):
+def percentiles_us(ms_values):
+    """median, p10 and p90 (and the extremes) of per-launch times given in ms, in us."""
+    import numpy as np
+    a = np.asarray(ms_values, dtype=np.float64) * 1e3
+    return {"launches": int(a.size), "median": round(float(np.median(a)), 2),
+            "p10": round(float(np.percentile(a, 10)), 2), "p90": round(float(np.percentile(a, 90)), 2),
+            "min": round(float(a.min()), 2), "max": round(float(a.max()), 2)}
+
+
+def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True, reps=20,
+               flush=False, load_policy="auto"):
     import numpy as np
     import torch
 
     import paged_kv_cache_53_amd as pkv
     import workloads as wl
     diag = min(10, steps)   # untimed pass that times every kernel of the step
-    cache, batch = build_batch(w, extra_tokens=steps + warmup + diag + 1, layout=layout, chunk_bytes=chunk_bytes)
+    extra = steps + warmup + diag + reps * (3 if flush else 1) + 1
+    cache, batch = build_batch(w, extra_tokens=extra, layout=layout, chunk_bytes=chunk_bytes)
+    if load_policy != "auto":
+        batch.load_policy = load_policy
     q = wl.q_values(w, device="cuda").contiguous()
     kn, vn = wl.new_token_kv(w, device="cuda")
     out = torch.empty_like(q)
@@ -185,6 +210,41 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
         one()
     torch.cuda.synchronize()
     kernels = pkv.timing_collect()
+    # per-launch distribution of the decode kernel: one step at a time, each collected on its own
+    # (untimed for `value`); with flush, each step follows a 1 GiB write that evicts L2 and MALL
+    pkv.timing_select(["decode"])
+    warm = []
+    for _ in range(reps):
+        one()
+        torch.cuda.synchronize()
+        n, ms = pkv.timing_collect()["decode"]
+        warm.append(ms / n)
+    cold = {}
+    if flush:
+        # after_write: each launch follows a 1 GiB write (L2 and MALL then hold the scratch's dirty
+        # lines); after_read: each follows a 1 GiB read (clean lines, as when other layers' KV was
+        # read in between)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for mode in ("after_write", "after_read"):
+            scratch.fill_(1)
+            scratch.view(torch.float32).amax()
+            torch.cuda.synchronize()
+            vals = []
+            for i in range(reps):
+                pkv.timing_enable(False)
+                if mode == "after_write":
+                    scratch.fill_((i + 2) & 0xFF)
+                else:
+                    scratch.view(torch.float32).amax()
+                torch.cuda.synchronize()
+                pkv.timing_enable(True)
+                one()
+                torch.cuda.synchronize()
+                n, ms = pkv.timing_collect()["decode"]
+                vals.append(ms / n)
+            cold[mode] = percentiles_us(vals)
+        del scratch
+    pkv.timing_select(None)
     pkv.timing_enable(False)
     total_s = t1 - t0
     # bytes: during step i every row attends over lens0 + i + 1 tokens (the appended one included)
@@ -196,7 +256,49 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
         tb += b
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     return {"total_s": total_s, "kv_bytes": kvb, "table_bytes": tb, "kernels": kernels, "steps": steps,
-            "lens0": lens0, "decode_timed": decode_timed, "diag_steps": diag}
+            "lens0": lens0, "decode_timed": decode_timed, "diag_steps": diag,
+            "decode_loads": ("cached" if batch._keep_cached() else "streamed") if layout == "paged" else "streamed",
+            "decode_launch_us": percentiles_us(warm) if warm else None,
+            "decode_launch_us_cold": cold or None}
+
+
+def _read_text(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def gpu_env():
+    """The device, its engine clock levels (sysfs, when readable) and the ROCm / HIP versions."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    env = {"device": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+           "rocm": _read_text("/opt/rocm/.info/version"), "torch_hip": torch.version.hip}
+    pci = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    txt = _read_text(f"/sys/bus/pci/devices/{pci}/pp_dpm_sclk")
+    env["sclk_mhz"] = None
+    if txt:
+        levels, cur = [], None
+        for ln in txt.splitlines():
+            parts = ln.replace(":", " ").split()
+            mhz = [int(x[:-3]) for x in parts if x.lower().endswith("mhz") and x[:-3].isdigit()]
+            if mhz:
+                levels.append(mhz[0])
+                if ln.rstrip().endswith("*"):
+                    cur = mhz[0]
+        if levels:
+            env["sclk_mhz"] = {"current": cur, "max": max(levels), "source": "pp_dpm_sclk after the timed region"}
+    return env
+
+
+def cpu_model():
+    txt = _read_text("/proc/cpuinfo") or ""
+    for ln in txt.splitlines():
+        if ln.startswith("model name"):
+            return ln.split(":", 1)[1].strip()
+    return None
 
 
 # Sources whose change invalidates measured HBM counters of the decode kernel.
@@ -389,7 +491,7 @@ def _oracle_sample(w, budget_s, cores, used):
         kvb += x
         tb += y
     return {"value": round((kvb + tb) / spent / 1e9, 4), "unit": "GB/s", "cores": int(used),
-            "kind": "oracle", "seqs_per_s": round(len(done) / spent, 3),
+            "kind": "oracle", "seqs_per_s": round(len(done) / spent, 3), "cpu_model": cpu_model(),
             "sample": f"{len(done)} of {w.num_seqs} rows of {w.name} (seeded order), "
                       f"{int(sum(int(w.seq_lens[r]) for r in done))} tokens, {spent:.1f} s of fp64 numpy "
                       f"(gather through the block table{' + dequantisation' if fp8 else ''} + attention), "
@@ -449,7 +551,8 @@ def main():
 
     w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
-                     chunk_bytes=args.chunk_bytes, fused=not args.unfused)
+                     chunk_bytes=args.chunk_bytes, fused=not args.unfused, reps=args.reps, flush=args.flush,
+                     load_policy=args.load_policy)
     total_s = res["total_s"]
     gbps = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
     seqs_s = w.num_seqs * args.steps / total_s
@@ -470,7 +573,14 @@ def main():
         "seqs_per_s": round(seqs_s, 1),
         "kernels": kern,
         "roofline": roofline(res, w),
+        "decode_loads": res["decode_loads"],
+        "decode_launch_us": res["decode_launch_us"],
+        "env": gpu_env(),
     }
+    if res["decode_launch_us_cold"] is not None:
+        line["decode_launch_us_cold"] = dict(res["decode_launch_us_cold"])
+        line["decode_launch_us_cold"]["note"] = ("each launch follows a 1 GiB write (after_write) or a 1 GiB "
+                                                 "read (after_read) that evicts L2 and the 256 MB Infinity Cache")
     if args.config == 4:
         # unique bytes: the shared prompt is stored (and mostly fetched from HBM) once
         prefix = 4000
@@ -606,7 +716,8 @@ def sweep(args):
             w = wl.build(5, block_size=B, placement=placement, partition_size=args.partition_size)
             key = placement if layout == "paged" else f"flat_{(chunk or 2 << 20) >> 10}KiB"
             try:
-                res = time_steps(w, args.steps, args.warmup, decode_only=True, layout=layout, chunk_bytes=chunk)
+                res = time_steps(w, args.steps, args.warmup, decode_only=True, layout=layout, chunk_bytes=chunk,
+                                 reps=0)
             except RuntimeError as e:      # a span pool that cannot map this many chunks
                 per[key] = {"error": str(e)}
                 log(f"B={B} {key}: {e}")

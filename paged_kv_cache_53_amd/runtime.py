@@ -152,24 +152,21 @@ class DecodeBatch:
         self.step_events = {}     # step index -> event recorded after that step
         self.slot_dev = torch.empty(self.S, dtype=torch.int64, device=dev)
         self.steps = 0
+        self.load_policy = "auto"   # "auto", "streamed" or "cached": how decode reads the pools
 
     STAGES = 8
     STAGE_EVENT_EVERY = 4
-    # An FP8 batch whose cached tokens take at most this many bytes decodes with cacheable loads: its
-    # KV then stays largely in the 256 MB Infinity Cache from one step to the next.  Larger batches
-    # stream with the non-temporal hint (bf16 streams at every size measured).
-    FP8_CACHEABLE_BYTES = 512 << 20
 
     def _keep_cached(self) -> bool:
-        """Decode with cacheable loads: blocks shared between rows, or a small FP8 batch.  On MI355X
-        an FP8 opt13b-class batch (0.36 GB) took 80.9 us cacheable against 82.9 us streamed, the
-        Llama-70B-class one (2.5 GB) 474 against 437 us; a bf16 opt13b-class batch 133 against 126 us."""
-        c = self.cache
-        if c.has_shared_blocks():
-            return True
-        if not c.quantised:
-            return False
-        return int(self.host_lens.sum()) * 2 * c.n_kv_heads * c.head_dim <= self.FP8_CACHEABLE_BYTES
+        """Decode with cacheable loads when blocks are shared between rows (their re-reads then hit
+        L2 and the Infinity Cache), else stream with the non-temporal hint.  Measured on MI355X,
+        decode us with each launch after a 1 GiB read / after a 1 GiB write: the shared-prefix swarm
+        88 / 143 cacheable against 120 / 120 streamed; without sharing, streamed loads were as fast
+        or faster (FP8 opt13b-class batch 86 / 87 against 86 / 128 cacheable, bf16 Llama-70B-class
+        764 / 772 against 840 / 904): cacheable loads evict dirty lines and pay their write-back."""
+        if self.load_policy != "auto":
+            return self.load_policy == "cached"
+        return self.cache.has_shared_blocks()
 
     def _stage_for(self, n: int) -> int:
         """The stage of step n, once the step that last read it (n - STAGES) has finished."""
