@@ -277,20 +277,26 @@ def gpu_env():
     env = {"device": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
            "rocm": _read_text("/opt/rocm/.info/version"), "torch_hip": torch.version.hip}
     pci = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
-    txt = _read_text(f"/sys/bus/pci/devices/{pci}/pp_dpm_sclk")
-    env["sclk_mhz"] = None
-    if txt:
-        levels, cur = [], None
-        for ln in txt.splitlines():
-            parts = ln.replace(":", " ").split()
-            mhz = [int(x[:-3]) for x in parts if x.lower().endswith("mhz") and x[:-3].isdigit()]
-            if mhz:
-                levels.append(mhz[0])
-                if ln.rstrip().endswith("*"):
-                    cur = mhz[0]
-        if levels:
-            env["sclk_mhz"] = {"current": cur, "max": max(levels), "source": "pp_dpm_sclk after the timed region"}
+    env["sclk_mhz"] = parse_dpm_sclk(_read_text(f"/sys/bus/pci/devices/{pci}/pp_dpm_sclk"))
     return env
+
+
+def parse_dpm_sclk(txt):
+    """{current, max} engine clock in MHz from the text of a pp_dpm_sclk file (one level a line,
+    "<index>: <n>Mhz", the active level marked with "*"), or None."""
+    if not txt:
+        return None
+    levels, cur = [], None
+    for ln in txt.splitlines():
+        parts = ln.replace(":", " ").split()
+        mhz = [int(x[:-3]) for x in parts if x.lower().endswith("mhz") and x[:-3].isdigit()]
+        if mhz:
+            levels.append(mhz[0])
+            if ln.rstrip().endswith("*"):
+                cur = mhz[0]
+    if not levels:
+        return None
+    return {"current": cur, "max": max(levels), "source": "pp_dpm_sclk after the timed region"}
 
 
 def cpu_model():
