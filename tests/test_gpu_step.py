@@ -162,13 +162,14 @@ def test_step_rejects_pageable_host_slots():
 @pytest.mark.parametrize("kv", ["native", "fp8"])
 def test_runtime_steps_fused_equal_unfused_with_forks(kv):
     """Twenty runtime steps over forked rows (copy-on-write on the first append into a shared,
-    partly filled block): the fused and the separate-call steps give the same bits every step.
-    Twenty steps cycle the batch's ring of slot stages more than twice, so stages are rewritten
-    after the step that read them has finished."""
+    partly filled block): the fused and the separate-call steps give the same bits every step, and
+    so does the fused step with the load policy forced to streamed loads (the runtime picks cacheable
+    loads for a batch with shared blocks).  Twenty steps cycle the batch's ring of slot stages more
+    than twice, so stages are rewritten after the step that read them has finished."""
     from paged_kv_cache_53_amd.runtime import DecodeBatch, PagedKVCache
     Hk, D, B, G = 2, 128, 16, 4
     outs, pools = {}, {}
-    for fused in (True, False):
+    for fused, policy in ((True, "auto"), (False, "auto"), (True, "streamed")):
         kw = dict(k_scale=0.02, v_scale=0.03) if kv == "fp8" else {}
         dt = torch.float8_e4m3fn if kv == "fp8" else torch.bfloat16
         cache = PagedKVCache(256, B, Hk, D, dt, device="cuda", fill="zero", **kw)
@@ -179,6 +180,8 @@ def test_runtime_steps_fused_equal_unfused_with_forks(kv):
             cache.fork(0, child)
         cache.append(3, prompt[:20], prompt[:20] * 2)
         batch = DecodeBatch(cache, [0, 1, 2, 3], G * Hk, 128, partition_size=32)
+        batch.load_policy = policy
+        assert batch._keep_cached() == (policy == "auto")   # forked rows share blocks
         seq = []
         for i in range(20):
             q = torch.randn(4, G * Hk, D, generator=g).to(torch.bfloat16).cuda()
@@ -188,13 +191,16 @@ def test_runtime_steps_fused_equal_unfused_with_forks(kv):
             batch.step(q, kn, vn, out, fused=fused)
             seq.append(out.clone())
         torch.cuda.synchronize()
-        outs[fused] = seq
-        pools[fused] = (cache.k_pool.clone(), cache.v_pool.clone(), batch.tables.clone(), batch.seq_lens.clone())
-    for x, y in zip(outs[True], outs[False]):
-        assert torch.equal(_bits(x), _bits(y))
-    for x, y in zip(pools[True], pools[False]):
-        assert torch.equal(_bits(x), _bits(y))
-    assert torch.isfinite(outs[True][-1].float()).all()
+        outs[(fused, policy)] = seq
+        pools[(fused, policy)] = (cache.k_pool.clone(), cache.v_pool.clone(), batch.tables.clone(),
+                                  batch.seq_lens.clone())
+    ref = (True, "auto")
+    for other in ((False, "auto"), (True, "streamed")):
+        for x, y in zip(outs[ref], outs[other]):
+            assert torch.equal(_bits(x), _bits(y)), other
+        for x, y in zip(pools[ref], pools[other]):
+            assert torch.equal(_bits(x), _bits(y)), other
+    assert torch.isfinite(outs[ref][-1].float()).all()
 
 
 def _sample_rows(w, n=6):
