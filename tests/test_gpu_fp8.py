@@ -12,7 +12,8 @@ import torch
 
 import paged_kv_cache_53_amd as pkv
 import workloads as wl
-from harness import TOL, TORCH_DTYPE, GpuState, log, max_abs_err, oracle_paged, oracle_rows
+from harness import (TOL, TORCH_DTYPE, GpuState, log, max_abs_err, max_abs_err_rows, oracle_all,
+                     oracle_paged, oracle_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -207,18 +208,36 @@ def test_fp8_runtime_decode_step_with_copy_on_write():
     assert cache.allocator.stats()["shared_blocks"] == 1     # the prompt's first full block
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5])
-def test_fp8_full_size_sampled_rows(cid):
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_fp8_full_size_all_rows(cid):
+    """The bench's FP8 launch (q-dtype output, the workload's own partition size) over the whole
+    batch, every element of every row against the oracle on the dequantised codes."""
     w = wl.quantised(wl.build(cid))
     log(f"full config {cid} fp8: {w.describe()}")
     st = GpuState(w, poison=True)
-    out = st.decode()                        # q-dtype output, the workload's partition size: the bench launch
-    assert torch.isfinite(out).all()
-    L = w.seq_lens
-    rows = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, w.num_seqs - 1})
-    ref = oracle_rows(w, rows)
-    err = max_abs_err(out, ref, rows=rows)
-    log(f"  rows {rows}: max abs err {err:.3e}")
-    assert err <= TOL[w.dtype], err
+    out = st.decode()
     del st
     torch.cuda.empty_cache()
+    err, row = max_abs_err_rows(out, oracle_all(w))
+    log(f"  all {w.num_seqs} rows: max abs err {err:.3e} (row {row}, L={int(w.seq_lens[row])})")
+    assert err <= TOL[w.dtype], err
+
+
+def test_fp8_full_size_shared_prefix_equals_copied_prefix_bitwise():
+    """The swarm on an FP8 cache at full size: shared prompt blocks and private copies of them decode
+    to the same bits, with either load policy; every row against the copied-prefix oracle."""
+    shared, copied = wl.quantised(wl.build(4)), wl.quantised(wl.build(4, copied_prefix=True))
+    a = GpuState(shared, poison=True)
+    assert a.alloc.stats()["shared_blocks"] == 250
+    oa, oa_cached = a.decode(), a.decode(shared_kv=True)
+    del a
+    torch.cuda.empty_cache()
+    b = GpuState(copied, poison=True)
+    ob = b.decode()
+    del b
+    torch.cuda.empty_cache()
+    assert torch.equal(oa.view(torch.int16).cpu(), ob.view(torch.int16).cpu())
+    assert torch.equal(oa_cached.view(torch.int16).cpu(), oa.view(torch.int16).cpu())
+    err, row = max_abs_err_rows(ob, oracle_all(copied))
+    log(f"config 4 full fp8, shared == copied bitwise; all rows: max abs err {err:.3e} (row {row})")
+    assert err <= TOL[copied.dtype], err

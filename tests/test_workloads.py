@@ -101,3 +101,16 @@ def test_bf16_storage_view_round_trip():
     t = torch.tensor([1.0, -0.0, 3.140625], dtype=torch.bfloat16)
     n = wl.storage_to_numpy(t)
     assert n.dtype == np.uint16 and n.tolist() == [0x3F80, 0x8000, 0x4049]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_host_draw_equals_int64_draw(dtype):
+    # the host's uint32 generator and the int64 form the GPU runs give the same elements, across
+    # chunk boundaries, at offsets past 2^32 (element counters wrap mod 2^32) and in the threaded case
+    key = wl._key(7, 2, 3)
+    for start, count in ((0, 1), (123, 1000), ((1 << 32) - 700, 2000), (5, 5 * wl._CPU_CHUNK + 17)):
+        a = wl._draw(key, start, count, dtype, "cpu")
+        b = wl._draw_torch(key, start, count, dtype, "cpu")
+        assert a.dtype == b.dtype and a.shape == b.shape
+        bits = torch.int32 if dtype == "f32" else torch.int16
+        assert torch.equal(a.view(bits), b.view(bits)), (start, count)

@@ -19,14 +19,17 @@ the CPU or on the GPU, with identical bits:
   quantiles Phi^-1((i + 0.5) / 65536) (scipy.special.ndtri in fp64, rounded
   to fp32 and then round-to-nearest-even to the storage dtype).
 
-All integer arithmetic stays below 2^49 in int64, so torch computes the same
-bits on any device.  Sequence lengths and block placement permutations come
+On a GPU the integer arithmetic runs in int64 torch operations that stay below
+2^49, so every device computes the same bits; on the host the same values come
+from wrapping uint32 numpy arithmetic on a thread pool, which is checked
+against the int64 form.  Sequence lengths and block placement permutations come
 from numpy.random.default_rng seeded with [seed, stream].
 """
 from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -357,10 +360,55 @@ def _key(seed: int, kind: int, source: int) -> int:
 
 
 _CHUNK = 1 << 25
+_CPU_CHUNK = 1 << 18
+
+
+def _hash32_u32(x: np.ndarray) -> np.ndarray:
+    """lowbias32 on a uint32 array in place (numpy's uint32 products wrap mod 2^32)."""
+    x ^= x >> np.uint32(16)
+    x *= np.uint32(0x7FEB352D)
+    x ^= x >> np.uint32(15)
+    x *= np.uint32(0x846CA68B)
+    x ^= x >> np.uint32(16)
+    return x
+
+
+def _draw_cpu(key: int, start: int, count: int, dtype: str) -> np.ndarray:
+    """``_draw`` on the host in storage form: the same elements from uint32 arithmetic, in
+    cache-sized chunks on a thread pool (numpy releases the GIL inside each operation)."""
+    from concurrent.futures import ThreadPoolExecutor
+    table = normal_table(dtype)
+    out = np.empty(count, dtype=table.dtype)
+
+    def fill(c0: int) -> None:
+        n = min(_CPU_CHUNK, count - c0)
+        e = np.arange(start + c0, start + c0 + n, dtype=np.uint64).astype(np.uint32)   # e mod 2^32
+        e *= np.uint32(_GOLDEN)
+        e += np.uint32(key)
+        out[c0:c0 + n] = table[_hash32_u32(e) >> np.uint32(16)]
+
+    starts = range(0, count, _CPU_CHUNK)
+    if count <= 4 * _CPU_CHUNK:
+        for c0 in starts:
+            fill(c0)
+    else:
+        with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+            list(ex.map(fill, starts))
+    return out
 
 
 def _draw(key: int, start: int, count: int, dtype: str, device):
     """Elements start..start+count-1 of the stream with this key, as a flat torch tensor."""
+    import torch
+    if str(device) == "cpu":
+        host = _draw_cpu(key, start, count, dtype)
+        t = torch.from_numpy(host.view(np.int16) if dtype == "bf16" else host)
+        return t.view(torch.bfloat16) if dtype == "bf16" else t
+    return _draw_torch(key, start, count, dtype, device)
+
+
+def _draw_torch(key: int, start: int, count: int, dtype: str, device):
+    """``_draw`` in int64 torch arithmetic on any device (the GPU path of the generator)."""
     import torch
     table_np = normal_table(dtype)
     if dtype == "bf16":
