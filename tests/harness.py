@@ -3,6 +3,7 @@ on the CPU -- from the same seeded inputs (workloads/).  Shared only by the test
 from __future__ import annotations
 
 import math
+import os
 import sys
 import time
 
@@ -15,9 +16,15 @@ TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
+PARITY: list = []   # every logged comparison with the oracle, printed again in the session summary
+
+
 def log(msg: str) -> None:
     print(f"[harness {time.strftime('%H:%M:%S')}] {msg}", flush=True)
     sys.stdout.flush()
+    if "err" in msg:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        PARITY.append(f"{test}: {msg.strip()}")
 
 
 # ------------------------------------------------------------------------------- GPU side
