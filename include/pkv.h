@@ -16,7 +16,9 @@
  * - Return value: PKV_OK or a negative PKV_ERR_* code.  Argument checks run
  *   before anything is launched or changed; a rejected call has no effect.
  * - Device pointers are caller-owned.  The library never allocates device
- *   memory: scratch space is the caller's workspace argument.
+ *   memory: scratch space is the caller's workspace argument, except for
+ *   pkv_paged_attention_decode_noalloc, whose scratch is a static device array
+ *   of the library (PKV_STATIC_SCRATCH_BYTES per GPU).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Launches are asynchronous on that stream; nothing here synchronises.
  *   A failed launch returns PKV_ERR_HIP.
@@ -51,7 +53,9 @@ enum {
   PKV_ERR_OOM = -2,         /* the allocator's pool has too few free blocks */
   PKV_ERR_NOT_FOUND = -3,   /* unknown sequence id */
   PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel for this head_dim / block_size / group */
-  PKV_ERR_HIP = -5          /* the HIP runtime reported an error */
+  PKV_ERR_HIP = -5,         /* the HIP runtime reported an error */
+  PKV_ERR_SCRATCH = -6      /* pkv_paged_attention_decode_noalloc: the call needs more scratch than
+                               PKV_STATIC_SCRATCH_BYTES */
 };
 
 enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 };
@@ -216,6 +220,30 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
                                   int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
                                   void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
                                   void* stream);
+
+/* ---- decode attention without allocation --------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  pkv_paged_attention_decode_ex with the same arguments, except that
+ * the plan, the counters and the partial results live in the library's own static scratch, a device
+ * array of PKV_STATIC_SCRATCH_BYTES on each GPU, instead of a workspace argument.  The call allocates
+ * nothing (no hipMalloc, no library allocation, no timing events); its first call on a device looks up
+ * that device's copy of the scratch (hipGetSymbolAddress), which the device then holds until the process
+ * ends.  Same kernels and the same bits as pkv_paged_attention_decode_ex.
+ *   - A call whose pkv_paged_attention_workspace_size() exceeds PKV_STATIC_SCRATCH_BYTES returns
+ *     PKV_ERR_SCRATCH before touching the device (128 MiB holds, e.g., 256 rows x 64 query heads x
+ *     128 dims up to 32768 tokens in 3072-token partitions, or 8 rows of 65536 tokens in 512-token
+ *     partitions).
+ *   - Every call on one GPU shares that GPU's scratch, and each call rewrites what it reads (no
+ *     clearing is needed between calls).  Two calls in flight at once on one GPU (other streams,
+ *     other threads) race on it: callers must order them.
+ * FP8 pools are not taken here (use pkv_paged_attention_decode_fp8 with a workspace). */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale, int32_t max_seq_len,
+                                       int32_t partition_size, int kv_dtype, uint32_t flags, void* stream);
 
 /* ---- quantised cache: FP8 E4M3 pools ------------------------------------------------
  * Quantising the cached keys and values is the memory lever the pages put after paging: an

@@ -23,13 +23,15 @@ from typing import List, Optional, Sequence, Tuple
 
 from . import _lib
 from ._lib import (PKV_BF16, PKV_ERR_HIP, PKV_ERR_INVALID, PKV_ERR_NOT_FOUND, PKV_ERR_OOM,  # noqa: F401
-                   PKV_ERR_UNSUPPORTED, PKV_F16, PKV_F32, PKV_FP8_E4M3, PKV_OK, KERNEL_NAMES, LibraryNotBuilt)
+                   PKV_ERR_SCRATCH, PKV_ERR_UNSUPPORTED, PKV_F16, PKV_F32, PKV_FP8_E4M3, PKV_OK,
+                   PKV_STATIC_SCRATCH_BYTES, KERNEL_NAMES, LibraryNotBuilt)
 
 __all__ = [
     "PKVError", "Allocator", "reshape_and_cache", "append_slots", "paged_attention_decode",
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
     "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
     "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks", "decode_step",
+    "paged_attention_decode_noalloc",
 ]
 
 
@@ -221,6 +223,28 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
         dtype_code(k_pool), flags, _stream(stream)),
         "pkv_paged_attention_decode_ex")
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                                   max_seq_len: int, partition_size: int = 512, stream=None,
+                                   shared_kv: bool = False) -> None:
+    """paged_attention_decode on 16-bit or fp32 pools with no workspace: the library's static device
+    scratch (PKV_STATIC_SCRATCH_BYTES per GPU) holds the plan and the partial results, and the call
+    allocates nothing (pkv_paged_attention_decode_noalloc).  Calls in flight at once on one GPU share
+    that scratch and must be ordered by the caller."""
+    N, Hk, D, B = _pool_dims(k_pool, v_pool)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [S, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [S, stride] with unit column stride")
+    if _is_fp8_pool(k_pool):
+        raise ValueError("FP8 pools take paged_attention_decode with a workspace")
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        _ptr(out), dtype_code(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        block_tables.stride(0), _ptr(seq_lens), S, Hq, Hk, D, B, N, float(scale), int(max_seq_len),
+        int(partition_size), dtype_code(k_pool), PKV_DECODE_SHARED_KV if shared_kv else 0, _stream(stream)),
+        "pkv_paged_attention_decode_noalloc")
 
 
 def decode_step(out, q, k, v, slot_mapping, k_pool, v_pool, block_tables, seq_lens, scale: float,

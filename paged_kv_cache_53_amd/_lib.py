@@ -8,6 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
+PKV_ERR_SCRATCH = -6
+PKV_STATIC_SCRATCH_BYTES = 128 << 20
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 KERNEL_NAMES = {0: "reshape_and_cache", 1: "append_slots", 2: "decode_plan", 3: "decode", 4: "decode_reduce",
                 5: "copy_blocks", 6: "swap_blocks", 7: "step_prologue"}
@@ -58,6 +60,8 @@ SIGNATURES = {
                                              C.c_float, I32, I32, P, SZ, C.c_int, P]),
     "pkv_paged_attention_decode_ex": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                                 C.c_float, I32, I32, P, SZ, C.c_int, C.c_uint32, P]),
+    "pkv_paged_attention_decode_noalloc": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                                     C.c_float, I32, I32, C.c_int, C.c_uint32, P]),
     "pkv_reshape_and_cache_fp8": (C.c_int, [P, P, P, I32, I64, I64, P, P, I32, I32, I32, I32, C.c_int,
                                             C.c_float, C.c_float, P]),
     "pkv_paged_attention_decode_fp8": (C.c_int, [P, C.c_int, P, C.c_int, P, P, C.c_float, C.c_float, P, I32, P,

@@ -160,6 +160,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_NOT_FOUND: return "unknown sequence";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or type";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_SCRATCH: return "needs more than the library's static scratch (PKV_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -449,24 +450,28 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
 
 // The launches of a prepared decode: the plan (unless a fused step's prologue made it), the
 // attention kernel, and the merge where some row has more than one partition.
-int decode_launch(const DecodeLaunch& L, bool plan, hipStream_t st) {
+// timed: record the optional per-kernel timing events (their creation allocates host-side event
+// objects, so the entry point that allocates nothing passes false).
+int decode_launch(const DecodeLaunch& L, bool plan, hipStream_t st, bool timed = true) {
   if (L.empty) return PKV_OK;
   const DecodeArgs& a = L.a;
+  auto before = [&](int k) { if (timed) timing_before(k, st); };
+  auto after = [&](int k) { if (timed) timing_after(k, st); };
   hipError_t e;
   if (plan) {
-    timing_before(PKV_K_DECODE_PLAN, st);
+    before(PKV_K_DECODE_PLAN);
     e = launch_decode_plan(a, L.kv_dtype, L.head_dim, st);
-    timing_after(PKV_K_DECODE_PLAN, st);
+    after(PKV_K_DECODE_PLAN);
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
-  timing_before(PKV_K_DECODE, st);
+  before(PKV_K_DECODE);
   e = launch_decode_main(a, L.kv_dtype, L.kv_fp8, L.head_dim, L.path, L.nt, L.grid, st);
-  timing_after(PKV_K_DECODE, st);
+  after(PKV_K_DECODE);
   if (e != hipSuccess) return PKV_ERR_HIP;
   if (a.max_parts > 1) {
-    timing_before(PKV_K_DECODE_REDUCE, st);
+    before(PKV_K_DECODE_REDUCE);
     e = launch_decode_reduce(a, L.kv_dtype, L.head_dim, st);
-    timing_after(PKV_K_DECODE_REDUCE, st);
+    after(PKV_K_DECODE_REDUCE);
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
@@ -487,9 +492,60 @@ int decode_impl(void* out, int out_dtype, const void* q, int q_dtype, const void
   return decode_launch(L, true, static_cast<hipStream_t>(stream));
 }
 
+// ---- the static scratch of pkv_paged_attention_decode_noalloc ---------------------------------
+// Device memory for the decode's plan, counters and partial results when the caller cannot
+// allocate: a file-scope device array of PKV_STATIC_SCRATCH_BYTES, one copy per GPU, held from the
+// code object's load on that GPU until the process ends.  In host code `scratch` names a host-side
+// stand-in, never device memory: only the address hipGetSymbolAddress returns for the current
+// device may reach a kernel.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};   // scratch's device address on each device, once looked up
+
+// The current device's copy of scratch; looked up once per device, with that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale, int32_t max_seq_len,
+                                       int32_t partition_size, int kv_dtype, uint32_t flags, void* stream) {
+  // the size check is plain arithmetic and comes first: a call that cannot fit touches no device
+  const size_t need = pkv_paged_attention_workspace_size(num_seqs, n_q_heads, head_dim, max_seq_len,
+                                                         partition_size);
+  if (need > PKV_STATIC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int r = scratch_address(&ws);
+  if (r != PKV_OK) return r;
+  DecodeLaunch L;
+  const int c = decode_prepare(&L, out, out_dtype, q, kv_dtype, k_pool, v_pool, false, 1.f, 1.f, block_tables,
+                               block_table_stride, seq_lens, num_seqs, n_q_heads, n_kv_heads, head_dim,
+                               block_size, num_blocks, scale, max_seq_len, partition_size, ws,
+                               PKV_STATIC_SCRATCH_BYTES, flags);
+  if (c != PKV_OK) return c;
+  // the plan kernel writes every counter and unit the attention reads, and every partial is written
+  // before the merge reads it, so nothing in scratch needs clearing between calls
+  return decode_launch(L, true, static_cast<hipStream_t>(stream), false);
+}
 
 int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,

@@ -271,3 +271,14 @@ def test_decode_step_args_layout_matches_the_header():
     want = [ctypes.sizeof(_lib.pkv_decode_step_args)] + [getattr(_lib.pkv_decode_step_args, f).offset
                                                           for f in fields]
     assert got == want
+
+
+def test_noalloc_decode_rejects_calls_beyond_its_static_scratch():
+    # the size check is host arithmetic and runs before the device is touched
+    lib = pkv.lib()
+    F16 = pkv.PKV_F16
+    assert pkv.workspace_size(2048, 64, 128, 32768, 512) > pkv.PKV_STATIC_SCRATCH_BYTES
+    r = lib.pkv_paged_attention_decode_noalloc(16, F16, 16, 16, 16, 16, 2048, 16, 2048, 64, 8, 128, 16, 100, 0.1,
+                                               32768, 512, F16, 0, None)
+    assert r == pkv.PKV_ERR_SCRATCH
+    assert "static scratch" in lib.pkv_status_string(pkv.PKV_ERR_SCRATCH).decode()
