@@ -91,6 +91,10 @@ def parse():
                    help="time the copy-on-write block copy kernel alone (4096 random block pairs)")
     p.add_argument("--swap", action="store_true",
                    help="time block moves between the pool and pinned host swap space (4096 blocks each way)")
+    p.add_argument("--read-ceiling", action="store_true",
+                   help="run only the streaming-read probe over its full sweep (one JSON line)")
+    p.add_argument("--no-read-ceiling", action="store_true",
+                   help="leave the short streaming-read probe out of the bench line")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                         "--copy-calibration into the traffic record (CPU only; writes --pmc-out)")
@@ -153,6 +157,23 @@ def kv_bytes(w, lens, table=True):
     return kv, tb
 
 
+def duplicate_tokens(tables, lens, block_size):
+    """Tokens the rows of a batch read from blocks that another row of the batch also reads, beyond the
+    first reading: every physical block's valid tokens count once towards the unique bytes HBM must
+    supply (a shared prompt is stored once), and the rest are re-reads.  tables: [S, >= ceil(L/B)] block
+    ids, lens: [S] lengths."""
+    seen = {}
+    total = 0
+    for s in range(len(lens)):
+        L = int(lens[s])
+        for i in range(-(-L // block_size)):
+            b = int(tables[s][i])
+            v = min(block_size, L - i * block_size)
+            seen[b] = max(seen.get(b, 0), v)
+            total += v
+    return total - sum(seen.values())
+
+
 # ------------------------------------------------------------------------------------- GPU timing
 def percentiles_us(ms_values):
     """median, p10 and p90 (and the extremes) of per-launch times given in ms, in us."""
@@ -193,6 +214,10 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
         one()
     torch.cuda.synchronize()
     lens0 = batch.host_lens.copy()
+    dup = 0
+    if layout == "paged":
+        tables0, _ = cache.allocator.fill_block_tables(batch.seq_ids, batch.stride, pad=0)
+        dup = duplicate_tokens(tables0, lens0, w.block_size)   # appends go to private blocks: constant
     # timed region: only the decode kernel carries an event pair (each pair costs the stream a few us)
     pkv.timing_select(["decode"])
     pkv.timing_enable(True)
@@ -255,7 +280,9 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
         kvb += a
         tb += b
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    per_token = 2 * w.n_kv_heads * w.head_dim * w.kv_esize
     return {"total_s": total_s, "kv_bytes": kvb, "table_bytes": tb, "kernels": kernels, "steps": steps,
+            "kv_bytes_unique": kvb - dup * per_token * steps, "duplicate_tokens": dup,
             "lens0": lens0, "decode_timed": decode_timed, "diag_steps": diag,
             "decode_loads": ("cached" if batch._keep_cached() else "streamed") if layout == "paged" else "streamed",
             "decode_launch_us": percentiles_us(warm) if warm else None,
@@ -349,7 +376,10 @@ def roofline(res, w=None):
     n_dec, ms_dec = res.get("decode_timed", (0, 0.0))
     if not n_dec:
         return None
-    per_launch = (res["kv_bytes"] + res["table_bytes"]) / res["steps"]
+    # unique bytes: a block read by several rows of the batch counts once (the shared prompt of a
+    # swarm is stored once); without sharing they equal the logical bytes
+    per_launch = (res["kv_bytes_unique"] + res["table_bytes"]) / res["steps"]
+    logical = (res["kv_bytes"] + res["table_bytes"]) / res["steps"]
     avg_s = ms_dec / n_dec / 1e3
     achieved = per_launch / avg_s / 1e9
     rec = measured_traffic(w) if w is not None else None
@@ -362,11 +392,50 @@ def roofline(res, w=None):
                      + ("FP8 E4M3 KV widened in registers" if w is not None and w.kv_format == "fp8" else "16-bit KV")
                      + ")",
            "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
+    if logical != per_launch:
+        out["achieved_logical"] = round(logical / avg_s / 1e9, 1)
+        out["bytes_per_launch_logical"] = int(logical)
     if rec:
         out["traffic_detail"] = {"fetch_bytes": int(rec["fetch_over_algorithmic"] * per_launch),
                                  "write_bytes": int(rec["write_over_algorithmic"] * per_launch),
                                  "source": os.path.relpath(traffic_record_path(w), ROOT)}
     return out
+
+
+def read_ceiling(full=False):
+    """The streaming-read ceiling: pkv_read_probe over a 4 GiB buffer (read once per launch, nothing
+    computed), timed with HIP events on the launch stream, over a sweep of waves per CU, loads per batch,
+    contiguous or scattered 4 KiB chunks, with and without the non-temporal hint.  Returns the best rate
+    and the sweep."""
+    import torch
+
+    import paged_kv_cache_53_amd as pkv
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    waves = (2, 4, 6, 8, 12, 16) if full else (4, 8)
+    loads = (4, 8, 16) if full else (8, 16)
+    modes = (0, 1, 2, 3) if full else (1, 3)
+    rows = []
+    for wpc in waves:
+        for nl in loads:
+            for mode in modes:
+                nbytes = pkv.read_probe(buf, wpc, nl, bool(mode & 1), bool(mode & 2), sink=sink)   # warm-up
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                reps = 5
+                ev[0].record()
+                for _ in range(reps):
+                    pkv.read_probe(buf, wpc, nl, bool(mode & 1), bool(mode & 2), sink=sink)
+                ev[1].record()
+                torch.cuda.synchronize()
+                us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+                rows.append({"waves_per_cu": wpc, "loads_per_batch": nl, "nontemporal": bool(mode & 1),
+                             "chunks": "scattered 4 KiB" if mode & 2 else "contiguous",
+                             "gbps": round(nbytes / (us * 1e-6) / 1e9, 1), "us": round(us, 1)})
+    del buf
+    best = max(rows, key=lambda r: r["gbps"])
+    return {"best_gbps": best["gbps"], "best": best, "sweep": rows if full else None,
+            "note": "pkv_read_probe: 4 GiB read once per launch by single-wave workgroups, 16 B per lane per "
+                    "load, two batches in flight per wave, no computation; mean of 5 launches per point"}
 
 
 # ------------------------------------------------------------------------------------- counters
@@ -550,6 +619,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
         return
 
+    if args.read_ceiling:
+        rc = read_ceiling(full=True)
+        print(json.dumps({"metric": "streaming HBM read GB/s (probe, no computation), 1×MI355X",
+                          "value": rc["best_gbps"], "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+                          "frac": round(rc["best_gbps"] / HBM_PEAK_GBPS, 4), **rc, "env": gpu_env()}), flush=True)
+        return
     if args.copy_blocks:
         return bench_copy_blocks(args)
     if args.swap:
@@ -560,7 +635,8 @@ def main():
                      chunk_bytes=args.chunk_bytes, fused=not args.unfused, reps=args.reps, flush=args.flush,
                      load_policy=args.load_policy)
     total_s = res["total_s"]
-    gbps = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
+    gbps = (res["kv_bytes_unique"] + res["table_bytes"]) / total_s / 1e9
+    gbps_logical = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
     seqs_s = w.num_seqs * args.steps / total_s
     kern = {k: {"launches": n, "avg_us": round(ms / n * 1e3, 2)} for k, (n, ms) in res["kernels"].items()}
     kern["_note"] = f"every kernel timed over {res['diag_steps']} untimed steps after the timed region"
@@ -587,11 +663,17 @@ def main():
         line["decode_launch_us_cold"] = dict(res["decode_launch_us_cold"])
         line["decode_launch_us_cold"]["note"] = ("each launch follows a 1 GiB write (after_write) or a 1 GiB "
                                                  "read (after_read) that evicts L2 and the 256 MB Infinity Cache")
-    if args.config == 4:
-        # unique bytes: the shared prompt is stored (and mostly fetched from HBM) once
-        prefix = 4000
-        uniq_tokens = prefix + int(sum(int(L) - prefix for L in res["lens0"]))
-        line["unique_kv_bytes_per_step"] = uniq_tokens * 2 * w.n_kv_heads * w.head_dim * w.kv_esize
+    if res["duplicate_tokens"]:
+        # rows share blocks: value and pct_hbm_peak count each block once (unique bytes); the rate over
+        # every row's own reading of its tokens is the logical one
+        line["value_logical"] = round(gbps_logical, 2)
+        line["bytes_note"] = (f"{res['duplicate_tokens']} tokens per step are read by more than one row; value, "
+                              "pct_hbm_peak and roofline count each physical block once (unique bytes)")
+    if not args.no_read_ceiling:
+        log("streaming-read probe ...")
+        rc = read_ceiling(full=False)
+        line["measured_read_gbps"] = rc["best_gbps"]
+        line["read_ceiling"] = {k: rc[k] for k in ("best", "note")}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)

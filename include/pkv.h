@@ -245,6 +245,22 @@ int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q, 
                                        int32_t block_size, int32_t num_blocks, float scale, int32_t max_seq_len,
                                        int32_t partition_size, int kv_dtype, uint32_t flags, void* stream);
 
+/* ---- measurement: the streaming-read ceiling ---------------------------------------------------
+ * Reads a device buffer once with waves shaped like the decode kernel's (one 64-lane wave per
+ * workgroup, 16 bytes per lane per load) and computes nothing on the data, so that the decode
+ * kernel's bandwidth can be set beside what HBM delivers to such waves on this GPU, next to the data
+ * sheet's figure.  Not part of the decode path.
+ *   buf, bytes      device buffer (16-byte aligned) and its size; at most `bytes` are read
+ *   waves_per_cu    1..32 single-wave workgroups per compute unit
+ *   loads_per_batch 4, 8 or 16 loads of 1 KiB per wave per batch; two batches in flight per wave
+ *   mode            bit 0: non-temporal loads; bit 1: 4 KiB chunks in a scattered order (as paged
+ *                   blocks are), else each wave reads one contiguous span
+ *   sink            device uint32 [1024], written only in a case that never arises (keeps the loads)
+ *   bytes_read      host, receives the bytes the launch reads (for the bandwidth)
+ * Asynchronous on `stream`; PKV_ERR_INVALID for a buffer too small for one batch of every wave. */
+int pkv_read_probe(const void* buf, size_t bytes, int32_t waves_per_cu, int32_t loads_per_batch, int mode,
+                   uint32_t* sink, size_t* bytes_read, void* stream);
+
 /* ---- quantised cache: FP8 E4M3 pools ------------------------------------------------
  * Quantising the cached keys and values is the memory lever the pages put after paging: an
  * 8-bit cache halves the bytes each sequence's attention reads ("Contiguous vs Paged KV Cache

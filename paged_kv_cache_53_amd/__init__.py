@@ -31,7 +31,7 @@ __all__ = [
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
     "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
     "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks", "decode_step",
-    "paged_attention_decode_noalloc",
+    "paged_attention_decode_noalloc", "read_probe",
 ]
 
 
@@ -513,3 +513,18 @@ class Allocator:
         buf = (C.c_int32 * max(n.value, 1))()
         _check(lib().pkv_free_list(self._h, buf, n.value, None), "pkv_free_list")
         return list(buf[:n.value])
+
+
+def read_probe(buf, waves_per_cu: int, loads_per_batch: int, nontemporal: bool = True, random_chunks: bool = False,
+               sink=None, stream=None) -> int:
+    """Launches the streaming-read probe over the device tensor buf (pkv_read_probe); returns the bytes
+    the launch reads.  sink: a device uint32 tensor of at least 1024 elements (allocated if None)."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(1024, dtype=torch.int32, device=buf.device)
+    n = C.c_size_t(0)
+    mode = (1 if nontemporal else 0) | (2 if random_chunks else 0)
+    _check(lib().pkv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), int(waves_per_cu),
+                                int(loads_per_batch), mode, _ptr(sink), C.byref(n), _stream(stream)),
+           "pkv_read_probe")
+    return int(n.value)

@@ -96,6 +96,7 @@ SIGNATURES = {
     "pkv_timing_enable": (C.c_int, [C.c_int]),
     "pkv_timing_collect": (C.c_int, [C.POINTER(pkv_kernel_time), I32, PI32]),
     "pkv_timing_select": (C.c_int, [C.c_uint32]),
+    "pkv_read_probe": (C.c_int, [P, SZ, I32, I32, C.c_int, P, C.POINTER(SZ), P]),
 }
 
 _lib = None

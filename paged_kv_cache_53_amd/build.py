@@ -25,7 +25,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["api.hip", "scatter.hip", "decode.hip", "span.hip"]
+HIP_SOURCES = ["api.hip", "scatter.hip", "decode.hip", "span.hip", "probe.hip"]
 HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              # keep a wave's work-claim atomic as written: the optimiser's rewrite reads the result
              # at once, making the wave wait for all of its outstanding loads

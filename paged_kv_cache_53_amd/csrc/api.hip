@@ -74,15 +74,15 @@ std::mutex cap_mu;
 std::unordered_map<int64_t, int32_t> cap_cache;
 
 hipError_t grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group, int block_size,
-                    int32_t* cap) {
+                    bool nt, int32_t* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4),
-  // the MFMA path one per storage type and one for flat spans
+  // the MFMA path one per storage type and one for flat spans, each for both cache policies
   const int variant = path == 1 ? (flat ? 5 : kv_fp8 ? 4 : 3) : (group == 1 ? 0 : group == 2 ? 1 : 2);
-  const int64_t key = ((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 8 + variant) * 64) +
-                      block_size;
+  const int64_t key = (((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 8 + variant) * 64) +
+                       block_size) * 2 + (nt ? 1 : 0);
   {
     std::lock_guard<std::mutex> g(cap_mu);
     auto it = cap_cache.find(key);
@@ -91,7 +91,7 @@ hipError_t grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, i
       return hipSuccess;
     }
   }
-  e = decode_main_grid_cap(dtype, kv_fp8, flat, head_dim, path, group, block_size, cap);
+  e = decode_main_grid_cap(dtype, kv_fp8, flat, head_dim, path, group, block_size, nt, cap);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> g(cap_mu);
   cap_cache[key] = *cap;
@@ -139,7 +139,7 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t n_q_heads, int32_t he
   const size_t parts = units * n_q_heads;
   w.counters_off = 0;
   w.units_off = 256;
-  w.m_off = round_up(w.units_off + units * sizeof(int2), 256);
+  w.m_off = round_up(w.units_off + units * sizeof(int4), 256);
   w.l_off = round_up(w.m_off + parts * sizeof(float), 256);
   w.acc_off = round_up(w.l_off + parts * sizeof(float), 256);
   w.total = round_up(w.acc_off + parts * head_dim * sizeof(float), 256);
@@ -417,7 +417,7 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.counters = reinterpret_cast<int32_t*>(ws + wl.counters_off);
-  a.units = reinterpret_cast<int2*>(ws + wl.units_off);
+  a.units = reinterpret_cast<int4*>(ws + wl.units_off);
   a.part_m = reinterpret_cast<float*>(ws + wl.m_off);
   a.part_l = reinterpret_cast<float*>(ws + wl.l_off);
   a.part_acc = reinterpret_cast<float*>(ws + wl.acc_off);
@@ -437,14 +437,15 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
   a.v_scale = kv_fp8 ? v_scale : 1.f;
   a.flat_bps = flat ? flat_bps : 0;
 
+  const bool nt = (flags & PKV_DECODE_SHARED_KV) == 0;
   int32_t cap = 0;
-  if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, &cap) != hipSuccess) return PKV_ERR_HIP;
+  if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, nt, &cap) != hipSuccess) return PKV_ERR_HIP;
   L->grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
   L->kv_dtype = kv_dtype;
   L->head_dim = head_dim;
   L->path = path;
   L->kv_fp8 = kv_fp8;
-  L->nt = (flags & PKV_DECODE_SHARED_KV) == 0;
+  L->nt = nt;
   return PKV_OK;
 }
 

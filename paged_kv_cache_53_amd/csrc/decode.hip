@@ -10,17 +10,22 @@
 //
 // How (MI355X design):
 // * Work unit = (row, KV head, partition of part_tokens tokens).  A one-workgroup
-//   plan kernel lists the (row, partition) pairs longest first; a persistent grid
-//   of single-wave workgroups takes units from one atomic counter, so no wave is
-//   launched for a partition that does not exist and long and short rows balance
-//   across the 256 CUs.
-// * A wave streams its units in tiles (16 tokens; 32 for an FP8 cache) through three register buffers,
-//   two tiles in flight: while tile t is computed, tiles t+1 and t+2 are loading.
-//   The issue side runs ahead across unit boundaries (it claims the next unit a
-//   few tiles before the current one ends and loads that unit's q), so HBM sees
-//   no gap between units.  When nothing real is left to issue it issues filler
-//   loads of an already-loaded tile, which keeps the number of loads per step
-//   fixed: the compiler's wait before a tile's use then covers that tile only.
+//   plan kernel lists the (row, partition) pairs longest first, each with its row
+//   length and first block id, so that opening a unit is one scalar load.  A
+//   persistent grid of single-wave workgroups takes the list's first rounds in a
+//   fixed order (round r: one unit per wave) and the rest from one atomic counter,
+//   so no wave is launched for a partition that does not exist and long and short
+//   rows balance across the 256 CUs.
+// * A wave streams its units in tiles (16 tokens; 32 for an FP8 cache) through NB
+//   register buffers, NB - 1 tiles in flight: while tile t is computed, tiles
+//   t+1 .. t+NB-1 are loading.  Streamed batches run one wave per SIMD with five
+//   buffers (FP8: four); batches whose rows share blocks run two waves per SIMD
+//   with three.  The issue side runs ahead across unit boundaries (it opens the
+//   next unit a few tiles before the current one ends and loads that unit's q
+//   straight into LDS), so HBM sees no gap between units.  When nothing real is
+//   left to issue it issues filler loads of an already-loaded tile, which keeps
+//   the number of loads per step fixed: the wait before a tile's use then covers
+//   that tile only.
 // * Block ids, lengths and the unit list are read with scalar loads, which wait
 //   on their own counter and never stall behind the vector loads.
 // * Key rows are stored as 16-byte vectors [c][token][X]: the 64 lanes of a
@@ -233,22 +238,33 @@ __device__ inline void plan_units(const DecodeArgs& a, int head_dim, LenOf len_o
   bucket_base[rb] = full_total + incl - cnt;
   bucket_fill[rb] = 0;
   if (tid == 0) a.counters[0] = full_total + part_total;
+  if (tid == 1) a.counters[17] = full_total;
   __syncthreads();
   const int64_t row_elems = static_cast<int64_t>(a.n_q_heads) * head_dim;
   for (int s = lo; s < hi; ++s) {
     const int L = len_of(s);
     const int nfull = L / P;
-    for (int p = 0; p < nfull; ++p) a.units[off + p] = make_int2(s, p);
+    for (int p = 0; p < nfull; ++p) a.units[off + p] = make_int4(s, p, L, 0);
     off += nfull;
     if (L % P) {
       const int bk = ((L % P) - 1) >> shift;
-      a.units[bucket_base[bk] + atomicAdd(&bucket_fill[bk], 1)] = make_int2(s, nfull);
+      a.units[bucket_base[bk] + atomicAdd(&bucket_fill[bk], 1)] = make_int4(s, nfull, L, 0);
     }
     if (L == 0) {  // empty row: zeros
       for (int64_t i = 0; i < row_elems; ++i) store1<T>(a.out, s * row_elems + i, 0.f, a.out_f32);
     }
   }
   if (tid >= 1 && tid <= 16) a.counters[tid] = 0;   // work-claim counters
+  // Second pass, one pair per thread at a time: the block id of each partition's first block, so that
+  // opening a unit is one scalar load.  (The workgroup barrier makes the first pass's stores visible.)
+  __syncthreads();
+  const int npairs = full_total + part_total;
+  for (int i = tid; i < npairs; i += 1024) {
+    const int4 u = a.units[i];
+    const int blk = (u.y * P) >> a.log2_block;
+    a.units[i].w = a.flat_bps > 0 ? a.block_tables[u.x] * a.flat_bps + blk
+                                  : a.block_tables[static_cast<int64_t>(u.x) * a.bt_stride + blk];
+  }
 }
 
 template <typename T>
@@ -355,7 +371,7 @@ __device__ inline void vload(unsigned& d, const void* p) {
 }
 // waits until at most N vector-memory operations are outstanding
 template <bool E, int N> __device__ inline void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  static_assert(!E || (N >= 0 && N < 64), "vmcnt holds 6 bits");
   if constexpr (E) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N));
 }
 // orders every later use of r after the preceding wait
@@ -386,23 +402,26 @@ struct Unit {
 
 // FLAT: the row's blocks are the consecutive blocks of its span (block_tables holds one span index
 // per row): the first block id is computed, not read from a table.
+// One scalar load of the unit's descriptor {row, partition, row length, first block id}, which the
+// plan wrote (FLAT: the first block id follows from the row's span, no table is read).
 template <typename T, bool FLAT>
 __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) {
   Unit<T> u;
   const int pair = id / a.n_kv_heads;
   u.kvh = id - pair * a.n_kv_heads;
-  u.s = ld_uniform(reinterpret_cast<const int32_t*>(a.units), 2 * static_cast<int64_t>(pair));
-  u.part = ld_uniform(reinterpret_cast<const int32_t*>(a.units), 2 * static_cast<int64_t>(pair) + 1);
-  const int L = row_len(a, u.s);
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 d = ((const __attribute__((address_space(4))) i32x4*)(a.units))[pair];
+  u.s = d.x;
+  u.part = d.y;
+  const int L = d.z;
   const int tok0 = u.part * a.part_tokens;
   u.ntok = min(a.part_tokens, L - tok0);
   u.nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  u.id_first = d.w;
   if constexpr (FLAT) {
     u.bt = a.block_tables;   // unused
-    u.id_first = ld_uniform(a.block_tables, u.s) * a.flat_bps + (tok0 >> a.log2_block);
   } else {
     u.bt = a.block_tables + static_cast<int64_t>(u.s) * a.bt_stride + (tok0 >> a.log2_block);
-    u.id_first = ld_uniform(u.bt, 0);
   }
   u.kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(u.kvh) * chunk;
   u.vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(u.kvh) * chunk;
@@ -549,6 +568,44 @@ __device__ inline void load_q_head(const DecodeArgs& a, int s, int hq, u32x4* qr
   }
 }
 
+// The LDS address (byte offset) of a __shared__ object.
+template <typename P>
+__device__ inline unsigned lds_offset(P* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) P*)p));
+}
+
+// 16 bytes per lane from g straight into LDS at lds_base + 16 * lane (a gfx950 global-to-LDS load):
+// no register receives the data, and the load counts on vmcnt like any other, so a wait that retires
+// a later load retires it too.  lds_base is wave-uniform.  M0, which holds the LDS address for the
+// instruction, is saved and restored around it; the nop covers the M0 write before its use.
+__device__ inline void lds_load16(const void* g, unsigned lds_base) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// load_q_head into LDS: lane (r16, g)'s q vector j goes to dst[j][lane], as load_q_head puts it in
+// qr[j] (the vectors of a head are NQ consecutive rows of 64 16-byte entries).
+template <typename T, typename KV, int D>
+__device__ inline void load_q_head_lds(const DecodeArgs& a, int s, int hq, u32x4 (*dst)[64]) {
+  constexpr int XQ = 16 / sizeof(T);
+  constexpr int R = Kv<KV>::X / XQ;
+  const int g = threadIdx.x >> 4;
+  const T* qrow = static_cast<const T*>(a.q) + (static_cast<int64_t>(s) * a.n_q_heads + hq) * D;
+#pragma unroll
+  for (int j = 0; j < D / XQ / 4; ++j) {
+    const int dim0 = Kv<KV>::X * (4 * (j / R) + g) + XQ * (j % R);
+    lds_load16(qrow + dim0, __builtin_amdgcn_readfirstlane(lds_offset(&dst[j][0])));
+  }
+}
+
 // the X elements of a 16-byte vector as floats
 template <typename T>
 __device__ inline void unpack16(const u32x4& v, float* o) {
@@ -641,6 +698,11 @@ struct MfmaMath {
   __device__ static void load_q(const DecodeArgs& a, const Unit<KV>& u, u32x4 (*qr)[NQ]) {
     const int r16 = threadIdx.x & 15;
     load_q_head<T, KV, D, kAsync>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), qr[0]);
+  }
+  // the same fragments straight into a unit's LDS slot
+  __device__ static void load_q_lds(const DecodeArgs& a, const Unit<KV>& u, u32x4 (*slot)[NQ][64]) {
+    const int r16 = threadIdx.x & 15;
+    load_q_head_lds<T, KV, D>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), slot[0]);
   }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     if constexpr (kQuant) compute32(R, q_lds, t0, ntok, scale_log2);
@@ -831,6 +893,11 @@ struct VecMath {
     for (int gi = 0; gi < GM; ++gi)
       load_q_head<T, T, D, kAsync>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), qr[gi]);
   }
+  __device__ static void load_q_lds(const DecodeArgs& a, const Unit<T>& u, u32x4 (*slot)[NQ][64]) {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi)
+      load_q_head_lds<T, T, D>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), slot[gi]);
+  }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     const bool partial = t0 + 16 > ntok;
@@ -935,30 +1002,36 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
       "s_mov_b64 exec, 1\n\t"
       "global_atomic_add %0, %2, %3, off sc0\n\t"
       "s_mov_b64 exec, %1"
-      : "+v"(slot), "=&s"(saved)
+      : "=&v"(slot), "=&s"(saved)
       : "v"(a.counters + 1), "v"(1));
 }
 
-// Persistent wave over a stream of tiles of the units it claims, with the loads of
-// the tile two steps ahead in flight while the current tile is computed (three tile buffers
-// in rotation).  The issue side runs up to one unit ahead of the compute side.  With
-// kPrefetchQ it loads that unit's q into registers before the unit's first tile loads and
-// parks it in the unit's LDS slot one step later, after that step's tile loads are issued, so
-// every wait in the steady state covers exactly the tile about to be used; otherwise q is
-// loaded and parked when the compute side reaches the unit.  When there is nothing left to
-// issue it re-issues the current tile's loads (a filler the compute side skips), so each step
-// issues the same loads on every path.  The next unit is claimed a few tiles before it is
-// needed.
-// KV: the storage type of the pools (the tile's element); Math carries the compute type.
-template <typename KV, int D, int Bsz, class Math, bool NT, bool FLAT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+// Persistent wave over a stream of tiles of the units it claims, with NB tile buffers in rotation:
+// while one tile is computed, the loads of the next NB - 1 are in flight.  The issue side runs up
+// to one unit ahead of the compute side.  When it enters a unit it loads that unit's q straight
+// into the unit's LDS slot (with kPrefetchQ; otherwise q is loaded when the compute side reaches
+// the unit), before the unit's first tile loads, so the wait that retires that tile retires q too.
+// When there is nothing left to issue it re-issues the current tile's loads (a filler the compute
+// side skips), so each step issues the same loads on every path.
+// The next unit is opened a few tiles before it is needed.  In the fixed rounds its index is known
+// and nothing waits; after them the wave claims it from the counter and reads the claim after
+// draining its loads, so the claim's result register never carries an in-flight value past that
+// block (a claim read some steps later has its register moved by the register allocator under the
+// pressure of five tile buffers, which the wait check reports).
+// KV: the storage type of the pools (the tile's element); Math carries the compute type; NB: tile
+// buffers; WPE: waves per SIMD the register budget is set for.
+template <typename KV, int D, int Bsz, class Math, bool NT, bool FLAT, int NB, int WPE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void decode_kernel(DecodeArgs a) {
   using Tile = typename Math::Tile;
   constexpr int TT = Tile::kTokens;   // tokens per tile
   constexpr int NQ = Math::NQ;
-  // explicitly waited loads while three tiles fit in 96 registers (32 per tile)
+  static_assert(NB >= 3 && NB <= 6, "tile buffers");
+  // explicitly waited loads while the tile buffers fit in registers (32 per tile)
   constexpr bool E = sizeof(Tile) <= 32 * 4;
   constexpr int LT = Tile::kLoads;   // every step issues exactly this many tile loads
+  static_assert(!E || (NB - 1) * LT < 64, "vmcnt holds 6 bits");
+  constexpr int kClaimAhead = 4;   // take the next unit this many tiles before it is needed
   const int64_t chunk = static_cast<int64_t>(D) * Bsz;
   const int64_t blk_stride = chunk * a.n_kv_heads;
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
@@ -975,84 +1048,86 @@ void decode_kernel(DecodeArgs a) {
   // (1 % faster on the Llama-70B-class and opt13b-class batches).  Cacheable (blocks shared between
   // rows): wave w starts on unit w, KV head w % 8, so XCD x reads head x of every row and keeps the
   // shared blocks' lines of that head in its L2 (the other order made the swarm 14 % slower).
-  int pending = 0;
-  const int first = (NT && !(gridDim.x & 7))
-                        ? static_cast<int>((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
-                        : static_cast<int>(blockIdx.x);
+  const int grid = static_cast<int>(gridDim.x);
+  const int first = (NT && !(grid & 7)) ? static_cast<int>((blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3))
+                                        : static_cast<int>(blockIdx.x);
+  // The first `rounds` units of every wave are fixed: round r gives wave w the unit at r * grid + first,
+  // so a wave opens them with no claim.  Fixed rounds cover only full partitions (units of one size)
+  // and at most three quarters of the units; the rest are handed out by the counter, which evens out
+  // waves that ran slower.
+  const int full_units = ld_uniform(a.counters, 17) * a.n_kv_heads;
+  const int rounds = max(1, min(full_units / grid, (3 * total) / (4 * grid)));
+  int round_i = 0;   // the fixed round of the issue cursor's unit
   if (first >= total) return;
   Unit<KV> uc = open_unit<KV, FLAT>(a, first, chunk);   // compute cursor
   Unit<KV> ui = uc;                              // issue cursor
   Unit<KV> un_next = uc;                         // the claimed unit after the issue cursor's
   u32x4 qr[Math::QH][NQ];
-  Math::template load_q<false>(a, uc, qr);
-#pragma unroll
-  for (int h = 0; h < Math::QH; ++h)
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) q_lds[0][h][j][threadIdx.x] = qr[h][j];
-  int slot_c = 0, slot_i = 0;
-  // Wave-uniform state bits, packed in one word: separate flags captured by the lambdas below
-  // get their stores merged through a pointer select, which puts them in scratch.
-  constexpr unsigned kAhead = 1;    // the issue cursor is in the unit after the compute cursor's
-  constexpr unsigned kEnded = 2;    // no more units to claim
-  constexpr unsigned kQPend = 4;    // qr holds the issue unit's q, not yet parked
-  constexpr unsigned kClaimed = 8;  // `pending` holds a claim whose result is not read yet
-  constexpr unsigned kNext = 16;    // un_next holds an opened unit the issue side has not reached
-  unsigned fl = 0;
-  int ti = 0, tc = 0;
-  constexpr int kClaimAhead = 4;   // claim the next unit this many tiles before it is needed
-
   auto park_q = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < Math::QH; ++h)
 #pragma unroll
       for (int j = 0; j < NQ; ++j) q_lds[slot][h][j][threadIdx.x] = qr[h][j];
   };
+  Math::template load_q<false>(a, uc, qr);   // the first unit's q: ordinary loads
+  park_q(0);
+  int slot_c = 0, slot_i = 0;
+  // Wave-uniform state bits, packed in one word: separate flags captured by the lambdas below
+  // get their stores merged through a pointer select, which puts them in scratch.
+  constexpr unsigned kAhead = 1;    // the issue cursor is in the unit after the compute cursor's
+  constexpr unsigned kEnded = 2;    // no more units to claim
+  constexpr unsigned kNext = 16;    // un_next holds an opened unit the issue side has not reached
+  unsigned fl = 0;
+  int ti = 0, tc = 0;
+
+  // Opens a claimed unit into un_next (its descriptor and first block id are dependent scalar reads,
+  // done a few tiles before the switch instead of on its path); got: the counter value the claim
+  // returned, read after a wait that retired it.
+  auto open_index = [&](int un) __attribute__((always_inline)) {
+    if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
+      un_next = open_unit<KV, FLAT>(a, un, chunk);
+      fl |= kNext;
+    } else {
+      fl |= kEnded;
+    }
+  };
+
 
   // Fills Y with the next tile of the issue stream; returns false when Y only holds filler
   // loads (nothing real left to issue right now) that the compute side must skip.
-  // tc_now: the compute cursor's tile offset, passed by value (a reference capture keeps tc in memory)
-  auto issue_next = [&](Tile& Y, int tc_now) __attribute__((always_inline)) -> bool {
-    // Opens a claimed unit into un_next (its descriptor and first block id are dependent scalar
-    // reads, done here a few tiles before the switch instead of on its path).
-    auto open_next = [&](int un) __attribute__((always_inline)) {
-      if (un >= 0 && un < total) {   // (a negative index can only be garbage: stop rather than fault)
-        un_next = open_unit<KV, FLAT>(a, un, chunk);
-        fl |= kNext;
-      } else {
-        fl |= kEnded;
-      }
-    };
-    if (fl & kClaimed) {
-      // the claim preceded an earlier step's LT tile loads: at most LT outstanding means it returned
-      vm_wait<E, LT>();
-      tie<E>(pending);
-      fl &= ~kClaimed;
-      open_next(__builtin_amdgcn_readfirstlane(pending) + static_cast<int>(gridDim.x));
+  // tc_now: the compute cursor's tile offset, passed by value (a reference capture keeps tc in memory).
+  // Takes the wave's next unit into un_next: the next fixed round's unit, or after the fixed rounds one
+  // from the counter.  A claim is read at once, after draining the wave's loads: the claim result's
+  // register then holds an in-flight value only inside this block.
+  auto take_next = [&]() __attribute__((always_inline)) {
+    if (round_i + 1 < rounds) {
+      ++round_i;
+      open_index(round_i * grid + first);
+    } else {
+      int got = 0;
+      claim_unit<E>(a, got);
+      vm_wait<E, 0>();
+      tie<E>(got);
+      open_index(__builtin_amdgcn_readfirstlane(got) + rounds * grid);
     }
+  };
+  auto issue_next = [&](Tile& Y, int tc_now) __attribute__((always_inline)) -> bool {
     if (ti >= ui.ntok && !(fl & (kAhead | kEnded))) {
-      if (!(fl & kNext)) {   // no claim was made ahead: claim now and drain
-        claim_unit<E>(a, pending);
-        vm_wait<E, 0>();
-        tie<E>(pending);
-        open_next(__builtin_amdgcn_readfirstlane(pending) + static_cast<int>(gridDim.x));
-      }
+      if (!(fl & kNext)) take_next();   // a unit shorter than the look-ahead
       if (fl & kNext) {
         ui = un_next;
         ti = 0;
         fl = (fl | kAhead) & ~kNext;
         slot_i = slot_c ^ 1;
-        if constexpr (Math::kPrefetchQ) {
-          Math::template load_q<E>(a, ui, qr);
-          fl |= kQPend;
-        }
+        // the unit's q goes straight into its LDS slot, ahead of the unit's first tile loads: the
+        // compute side reads the slot only after the wait that retires that tile (slot_i belongs to
+        // a unit the compute side has finished)
+        if constexpr (Math::kPrefetchQ) Math::load_q_lds(a, ui, q_lds[slot_i]);
       }
     }
     const bool is_real = ti < ui.ntok;
-    // the claim goes before this step's tile loads, so they count towards its wait
-    if (is_real && !(fl & (kClaimed | kNext | kEnded)) && ui.ntok - (ti + TT) <= kClaimAhead * TT) {
-      claim_unit<E>(a, pending);
-      fl |= kClaimed;
-    }
+    // open the next unit a few tiles before it is needed (its descriptor is a dependent scalar load)
+    if (is_real && !(fl & (kNext | kEnded)) && ui.ntok - (ti + TT) <= kClaimAhead * TT) take_next();
     // One load sequence on every path (a filler re-reads the compute cursor's tile, which keeps
     // the per-step loads uniform): separate sequences would meet in a merge that the compiler
     // may resolve by copying the loaded registers before the data arrives.
@@ -1066,35 +1141,27 @@ void decode_kernel(DecodeArgs a) {
     return is_real;
   };
 
-  Tile A{}, B{}, C{};   // defined before their first load, which names them as in/out operands
-  // bit i set: buffer i (A, B, C) holds a real tile of the compute unit, clear: a filler
+  Tile buf[NB] = {};   // defined before their first load, which names them as in/out operands
+  // bit i set: buffer i holds a real tile of the compute unit, clear: a filler
   unsigned real = 0;
-  real |= issue_next(A, 0) ? 1u : 0u;
-  real |= issue_next(B, 0) ? 2u : 0u;
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) real |= issue_next(buf[i], 0) ? (1u << i) : 0u;
 
   Math mt;
   mt.reset();
   if constexpr (!Math::kPrefetchQ) mt.group = a.group;
   const float scale_log2 = a.scale_log2;
 
-  // X: the buffer issued two steps ago; Y gets the next issue.  XI / YI are their bit positions.
-  auto step = [&](Tile& X, auto xi, Tile& Y, auto yi) __attribute__((always_inline)) -> bool {
-    constexpr unsigned XB = 1u << decltype(xi)::value, YB = 1u << decltype(yi)::value;
-    if constexpr (Math::kPrefetchQ) {
-      if (fl & kQPend) {   // loaded a step ago, before that step's LT tile loads
-        vm_wait<E, LT>();
-#pragma unroll
-        for (int h = 0; h < Math::QH; ++h)
-#pragma unroll
-          for (int j = 0; j < NQ; ++j) tie<E>(qr[h][j]);
-        park_q(slot_i);
-        fl &= ~kQPend;
-      }
-    }
+  // Step `xi` of the unrolled loop: computes buffer xi (issued NB - 1 steps ago) and issues the next
+  // tile into buffer yi (computed one step ago).
+  auto step = [&](auto xi, auto yi) __attribute__((always_inline)) -> bool {
+    constexpr int XI = decltype(xi)::value, YI = decltype(yi)::value;
+    constexpr unsigned XB = 1u << XI, YB = 1u << YI;
+    Tile& X = buf[XI];
     const bool x_real = (real & XB) != 0;
-    real = issue_next(Y, tc) ? (real | YB) : (real & ~YB);
-    // X was issued two steps ago; each of the two steps since issued LT tile loads
-    vm_wait<E, 2 * LT>();
+    real = issue_next(buf[YI], tc) ? (real | YB) : (real & ~YB);
+    // X was issued NB - 1 steps ago; each of the steps since issued LT tile loads
+    vm_wait<E, (NB - 1) * LT>();
     X.template tie_all<E>();
     if (!x_real) return true;   // a filler: nothing to compute this step
     mt.compute(X, q_lds[slot_c], tc, uc.ntok, scale_log2);
@@ -1113,14 +1180,22 @@ void decode_kernel(DecodeArgs a) {
     }
     return true;
   };
+  // step i computes buffer i and issues into buffer i - 1 (mod NB)
+  auto steps = [&](auto... is) __attribute__((always_inline)) {
+    for (;;) {
+      if (!(step(is, std::integral_constant<int, (decltype(is)::value + NB - 1) % NB>{}) && ...)) break;
+    }
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  for (;;) {
-    if (!step(A, I0{}, C, I2{})) break;
-    if (!step(B, I1{}, A, I0{})) break;
-    if (!step(C, I2{}, B, I1{})) break;
-  }
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  if constexpr (NB == 3) steps(I0{}, I1{}, I2{});
+  else if constexpr (NB == 4) steps(I0{}, I1{}, I2{}, I3{});
+  else if constexpr (NB == 5) steps(I0{}, I1{}, I2{}, I3{}, I4{});
+  else steps(I0{}, I1{}, I2{}, I3{}, I4{}, I5{});
   vm_wait<E, 0>();   // filler loads still in flight land before the wave ends
 }
 
@@ -1173,12 +1248,33 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
+// Tile buffers and waves per SIMD of each kernel variant.
+#ifndef PKV_NB16
+#define PKV_NB16 5
+#endif
+#ifndef PKV_WPE16
+#define PKV_WPE16 1
+#endif
+#ifndef PKV_NB8
+#define PKV_NB8 4
+#endif
+#ifndef PKV_WPE8
+#define PKV_WPE8 1
+#endif
+template <typename KV, class Math, bool NT> struct Pipeline {
+  static constexpr bool k16 = sizeof(KV) == 2 && NT;   // streamed 16-bit pools on MFMA
+  static constexpr bool k8 = std::is_same<KV, E4M3>::value && NT;
+  static constexpr int NB = k16 ? PKV_NB16 : k8 ? PKV_NB8 : 3;
+  static constexpr int WPE = k16 ? PKV_WPE16 : k8 ? PKV_WPE8 : 2;
+};
+
 template <typename KV, int D, class Math, bool NT, bool FLAT = false>
 const void* kernel_ptr_b(int block_size) {
+  constexpr int NB = Pipeline<KV, Math, NT>::NB, W = Pipeline<KV, Math, NT>::WPE;
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT, FLAT>);
-    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT, FLAT>);
-    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT, FLAT>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT, FLAT, NB, W>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT, FLAT, NB, W>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT, FLAT, NB, W>);
     default: return nullptr;
   }
 }
@@ -1280,12 +1376,12 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 }
 
 hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
-                                int block_size, int32_t* cap) {
-  // both cache policies compile to the same code shape: the streamed variant stands for both
+                                int block_size, bool nt, int32_t* cap) {
+  // the two cache policies have their own pipeline shapes, so their own occupancy
   const void* fn =
-      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, true, kv_fp8, flat)
-      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, true, kv_fp8, flat)
-                         : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, true, kv_fp8, flat);
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, nt, kv_fp8, flat)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, nt, kv_fp8, flat)
+                         : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, nt, kv_fp8, flat);
   if (!fn) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -34,9 +34,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   // workspace views
-  int32_t* counters;     // [0] = number of (row, partition) units, [1] = units handed out after the
-                         // first gridDim.x, which the waves of the persistent grid start on
-  int2* units;           // (row, partition) pairs, row-major, partitions ascending
+  int32_t* counters;     // [0] = number of (row, partition) units, [1] = units handed out by claim
+                         // after the ones the waves of the persistent grid take in fixed rounds
+  int4* units;           // per (row, partition) pair, largest first: {row, partition, row length,
+                         // block id of the partition's first block}
   float* part_m;         // [S][Hq][max_parts]  running max of x*log2(e)
   float* part_l;         // [S][Hq][max_parts]  sum of weights
   float* part_acc;       // [S][Hq][max_parts][D]  unnormalised weighted V
@@ -103,7 +104,7 @@ hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int h
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.
 hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
-                                int block_size, int32_t* cap);
+                                int block_size, bool nt, int32_t* cap);
 
 // Physical memory of a flat-span pool is mapped in chunks of this size unless the caller picks another.
 constexpr size_t PKV_SPAN_DEFAULT_CHUNK = size_t{2} << 20;

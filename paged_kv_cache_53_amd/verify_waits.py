@@ -29,15 +29,23 @@ _MAX_CTX = 256   # flag contexts kept apart per block before falling back to one
 _CAP = 64  # vmcnt is 6 bits: an operation with 64 issued after it has retired under any wait
 _STORE = ("global_store", "buffer_store", "scratch_store", "flat_store")
 _VMEM = ("global_", "buffer_", "scratch_", "flat_")
+_TO_LDS = ("global_load_lds_", "buffer_load_lds_", "scratch_load_lds_")
+
+
+_AGPR = 1024   # accumulation registers a0.. are tracked as _AGPR + index
 
 
 def _regs(tok: str) -> Set[int]:
+    """Vector registers named by an operand: v-registers by index, a-registers as _AGPR + index."""
     tok = tok.rstrip(",")
-    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
     if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"v(\d+)$", tok)
-    return {int(m.group(1))} if m else set()
+        base = _AGPR if m.group(1) == "a" else 0
+        return set(range(base + int(m.group(2)), base + int(m.group(3)) + 1))
+    m = re.match(r"([va])(\d+)$", tok)
+    if not m:
+        return set()
+    return {(_AGPR if m.group(1) == "a" else 0) + int(m.group(2))}
 
 
 class _Insn:
@@ -52,7 +60,8 @@ class _Insn:
         self.vmem = self.op.startswith(_VMEM)
         m = re.search(r"vmcnt\((\d+)\)", text) if self.op == "s_waitcnt" else None
         self.wait = int(m.group(1)) if m else None
-        if self.op.startswith(_STORE):
+        if self.op.startswith(_STORE) or self.op.startswith(_TO_LDS) or self.op.endswith("_lds"):
+            # stores, and loads that deliver straight into LDS: every register operand is a source
             self.writes, self.reads = set(), set().union(*[_regs(o) for o in ops]) if ops else set()
         elif ops:
             self.writes = _regs(ops[0])
@@ -60,7 +69,7 @@ class _Insn:
         else:
             self.writes, self.reads = set(), set()
         # destinations whose arrival the kernel waits for explicitly
-        self.asm_dst = self.writes if (asm and self.vmem and not self.op.startswith(_STORE)) else set()
+        self.asm_dst = self.writes if (asm and self.vmem and self.writes) else set()
 
 
 def _kernel_blocks(body: List[str]):
@@ -198,6 +207,12 @@ _NO_DEF = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "
            "s_setprio", "s_sleep", "s_sendmsg", "s_setpc", "s_trap", "s_dcache")
 
 
+# VOP3b instructions: vector destination first, then a scalar carry-out (or a scale flag) that the
+# instruction writes
+_VOP3B = ("v_mad_u64_u32", "v_mad_i64_i32", "v_add_co_u32", "v_sub_co_u32", "v_subrev_co_u32",
+          "v_addc_co_u32", "v_subb_co_u32", "v_subbrev_co_u32", "v_div_scale_f32", "v_div_scale_f64")
+
+
 def _sgpr_use_def(ins: "_Insn") -> Tuple[Set[int], Set[int]]:
     """Conservative SGPR reads (over-approximated) and definitions (under-approximated)."""
     toks = ins.text.replace(",", " ").split()[1:]
@@ -207,12 +222,13 @@ def _sgpr_use_def(ins: "_Insn") -> Tuple[Set[int], Set[int]]:
         (op.startswith("s_") and not op.startswith(_NO_DEF) and not op.startswith(("s_store", "s_buffer_store")))
         or op in ("v_readfirstlane_b32", "v_readlane_b32")
         or (op.startswith("v_cmp_") and op.endswith("_e64")))
-    d = set(regs[0]) if (defines_first and regs) else set()
+    defined = {0} if defines_first else set()
+    if not ins.asm and op.startswith(_VOP3B):
+        defined = {1}
+    d: Set[int] = set()
     u: Set[int] = set()
     for i, r in enumerate(regs):
-        if i == 0 and defines_first:
-            continue
-        u.update(r)
+        (d if i in defined else u).update(r)
     return u, d
 
 
@@ -260,7 +276,9 @@ def check_kernel(body: List[str]) -> List[str]:
                 else:
                     consts.pop(-2, None)
                 if bad:
-                    reports.add(f"{lab}: '{ins.text}' touches v{min(bad)} while its explicitly waited load may be in flight")
+                    r = min(bad)
+                    name = f"a{r - _AGPR}" if r >= _AGPR else f"v{r}"
+                    reports.add(f"{lab}: '{ins.text}' touches {name} while its explicitly waited load may be in flight")
                 _step_consts(ins, consts, flags)
             else:
                 # asm may write any sgpr it names: forget flag values it touches

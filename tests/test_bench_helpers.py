@@ -40,3 +40,28 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_duplicate_tokens_counts_shared_blocks_once():
+    # a tiny swarm through the oracle's allocator: a 40-token prompt (blocks of 16: two full, one with 8),
+    # three children sharing its first 32 tokens, each with a private suffix; the third child shares
+    # only the first block
+    from oracle.allocator import BlockAllocatorModel
+    B = 16
+    a = BlockAllocatorModel(64, B)
+    a.alloc(9, 40)
+    for c in (0, 1):
+        a.fork(9, c, 32)
+    a.fork(9, 2, 16)
+    a.alloc(0, 5)
+    a.alloc(1, 20)
+    a.alloc(2, 1)
+    rows = [9, 0, 1, 2]
+    lens = [40, 37, 52, 17]
+    tables = [a.block_table(r) for r in rows]
+    # logical tokens 146; unique: the parent's 40, child 0's own 5, child 1's own 20, child 2's own 1
+    assert bench.duplicate_tokens(tables, lens, B) == 146 - (40 + 5 + 20 + 1)
+    # no sharing: nothing is counted twice
+    assert bench.duplicate_tokens([[0, 1], [2]], [20, 9], B) == 0
+    # a shared partial block counts its longest reader's valid tokens once
+    assert bench.duplicate_tokens([[0, 1], [0, 1]], [24, 20], B) == 16 + 4

@@ -48,3 +48,24 @@ def test_bench_line_has_the_contract_fields():
     cold = d["decode_launch_us_cold"]
     assert cold["after_write"]["launches"] == 3 and cold["after_read"]["launches"] == 3
     assert d["env"]["arch"].startswith("gfx950")
+    # the streaming-read probe's best rate, beside the data sheet's 8 TB/s
+    assert 0 < d["measured_read_gbps"] < 8000.0
+    assert d["read_ceiling"]["best"]["gbps"] == d["measured_read_gbps"]
+
+
+def test_bench_counts_a_shared_prompt_once():
+    """The swarm (20 rows sharing a 4000-token prompt): value, pct_hbm_peak and the roofline count each
+    shared block once, and the logical rate, over every row's own reading, is reported beside it."""
+    cmd = [sys.executable, "-u", str(ROOT / "bench.py"), "--config", "4", "--steps", "3", "--warmup", "1",
+           "--reps", "2", "--no-cpu-baseline", "--no-read-ceiling"]
+    print("bench swarm run:", " ".join(cmd[2:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=str(ROOT))
+    assert r.returncode == 0, r.stderr[-3000:]
+    d = json.loads([ln for ln in r.stdout.splitlines() if ln.strip()][0])
+    roof = d["roofline"]
+    # 19 of the 20 rows re-read the prompt's 4000 tokens: logical bytes exceed unique ones by that much
+    per_token = 2 * 8 * 128 * 2
+    assert roof["bytes_per_launch_logical"] - roof["bytes_per_launch"] == 19 * 4000 * per_token
+    assert d["value_logical"] > d["value"]
+    assert d["pct_hbm_peak"] == pytest.approx(100 * d["value"] / 8000.0, abs=0.01)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-3)

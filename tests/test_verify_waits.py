@@ -136,6 +136,51 @@ def test_scalar_read_from_in_flight_register_must_stay_unused():
     assert len(_check(used)) == 1
 
 
+def test_carry_out_of_a_vop3b_instruction_is_a_definition():
+    # v_mad_i64_i32 writes its second operand (the carry-out): a poisoned scalar there is overwritten,
+    # not used; its scalar sources are still uses
+    body = f"""
+{_asm("global_atomic_add v4, v[0:1], v2, off sc0")}
+\tv_readfirstlane_b32 s6, v4
+\tv_mad_i64_i32 v[10:11], s[6:7], v1, s8, v[12:13]
+\ts_cmp_ge_i32 s6, 3
+\ts_endpgm
+"""
+    assert _check(body) == []
+    as_source = body.replace("v_mad_i64_i32 v[10:11], s[6:7], v1, s8,", "v_mad_i64_i32 v[10:11], s[2:3], v1, s6,")
+    assert len(_check(as_source)) == 2      # the mad and the compare both read s6
+
+
+def test_load_into_lds_has_no_register_destination():
+    # global_load_lds_dwordx4 reads its address registers and writes LDS only: reusing the address
+    # registers afterwards is not a use of in-flight data, but it still counts towards vmcnt
+    body = f"""
+{_asm("global_load_dwordx4 v[4:7], v[0:1], off")}
+{_asm("s_mov_b32 m0, s2")}
+{_asm("global_load_lds_dwordx4 v[8:9], off")}
+\tv_mov_b32_e32 v8, 0
+{_asm("s_waitcnt vmcnt(1)")}
+\tv_mov_b32_e32 v20, v4
+\ts_endpgm
+"""
+    assert _check(body) == []
+    too_early = body.replace("vmcnt(1)", "vmcnt(2)")
+    assert len(_check(too_early)) == 1
+
+
+def test_accumulation_registers_are_tracked():
+    body = f"""
+{_asm("global_atomic_add a4, v[0:1], v2, off sc0")}
+\tv_accvgpr_read_b32 v8, a4
+\ts_endpgm
+"""
+    assert len(_check(body)) == 1
+    waited = body.replace("\tv_accvgpr_read_b32", _asm("s_waitcnt vmcnt(0)") + "\n\tv_accvgpr_read_b32")
+    assert _check(waited) == []
+    # a4 and v4 are different registers
+    assert _check(body.replace("v_accvgpr_read_b32 v8, a4", "v_mov_b32_e32 v8, v4")) == []
+
+
 def test_built_decode_kernels_pass():
     path = os.path.join(ROOT, "paged_kv_cache_53_amd", "_build", "decode.s")
     if not os.path.exists(path):
