@@ -91,6 +91,8 @@ def parse():
                    help="time the copy-on-write block copy kernel alone (4096 random block pairs)")
     p.add_argument("--swap", action="store_true",
                    help="time block moves between the pool and pinned host swap space (4096 blocks each way)")
+    p.add_argument("--math", default="mfma", choices=["mfma", "vector"],
+                   help="with --decode-only: vector = the per-token vector path (16-bit KV, one head per KV head)")
     p.add_argument("--read-ceiling", action="store_true",
                    help="run only the streaming-read probe over its full sweep (one JSON line)")
     p.add_argument("--no-read-ceiling", action="store_true",
@@ -185,7 +187,7 @@ def percentiles_us(ms_values):
 
 
 def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True, reps=20,
-               flush=False, load_policy="auto"):
+               flush=False, load_policy="auto", math="mfma"):
     import numpy as np
     import torch
 
@@ -196,6 +198,10 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
     cache, batch = build_batch(w, extra_tokens=extra, layout=layout, chunk_bytes=chunk_bytes)
     if load_policy != "auto":
         batch.load_policy = load_policy
+    if math == "vector":
+        if not decode_only or layout != "paged":
+            raise SystemExit("--math vector times the paged decode call alone (--decode-only)")
+        batch.vector = True
     q = wl.q_values(w, device="cuda").contiguous()
     kn, vn = wl.new_token_kv(w, device="cuda")
     out = torch.empty_like(q)
@@ -633,7 +639,7 @@ def main():
     w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
                      chunk_bytes=args.chunk_bytes, fused=not args.unfused, reps=args.reps, flush=args.flush,
-                     load_policy=args.load_policy)
+                     load_policy=args.load_policy, math=args.math)
     total_s = res["total_s"]
     gbps = (res["kv_bytes_unique"] + res["table_bytes"]) / total_s / 1e9
     gbps_logical = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
@@ -656,6 +662,7 @@ def main():
         "kernels": kern,
         "roofline": roofline(res, w),
         "decode_loads": res["decode_loads"],
+        "decode_math": args.math,
         "decode_launch_us": res["decode_launch_us"],
         "env": gpu_env(),
     }

@@ -211,8 +211,12 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
  *                         rows that reread them hit in L2 / the Infinity Cache.  Without it
  *                         the tiles are streamed with the non-temporal hint, which is faster
  *                         when every block is read once.  It changes no result.
+ *   PKV_DECODE_VECTOR     16-bit KV with G = 1 (multi-head attention): per-token fp32 dot products
+ *                         with cross-lane reductions and fp32 weights, instead of MFMA with the one
+ *                         head padded to 16 (within the same tolerance of the exact result, not the
+ *                         same bits); PKV_ERR_UNSUPPORTED for G > 1, FP8 pools and flat spans.
  * Unknown flag bits: PKV_ERR_INVALID. */
-enum { PKV_DECODE_SHARED_KV = 1 };
+enum { PKV_DECODE_SHARED_KV = 1, PKV_DECODE_VECTOR = 2 };
 int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables, int32_t block_table_stride,
                                   const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,

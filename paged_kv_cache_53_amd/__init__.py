@@ -183,15 +183,17 @@ def workspace_size(num_seqs, n_q_heads, head_dim, max_seq_len, partition_size=51
 
 
 PKV_DECODE_SHARED_KV = 1
+PKV_DECODE_VECTOR = 2
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
                            partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False,
-                           k_scale=None, v_scale=None) -> None:
+                           k_scale=None, v_scale=None, vector: bool = False) -> None:
     """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h).
 
     shared_kv: some blocks are read by more than one row (forks, a shared prompt); keeps them
     cacheable instead of streaming them.  Results are the same either way.
+    vector: 16-bit KV with one query head per KV head on the per-token vector path instead of MFMA.
     FP8 pools (float8_e4m3fn / uint8): attention over k_scale * value(code) and
     v_scale * value(code), with q in bf16 or f16."""
     import torch
@@ -204,7 +206,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
     need = workspace_size(S, Hq, D, max_seq_len, partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    flags = PKV_DECODE_SHARED_KV if shared_kv else 0
+    flags = (PKV_DECODE_SHARED_KV if shared_kv else 0) | (PKV_DECODE_VECTOR if vector else 0)
     if _is_fp8_pool(k_pool):
         if k_scale is None or v_scale is None:
             raise ValueError("an FP8 cache needs k_scale and v_scale")

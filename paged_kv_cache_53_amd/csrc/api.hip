@@ -363,7 +363,7 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
   L->empty = false;
   const int kv_dtype = q_dtype;   // the compute type of the kernels
   const bool flat = flat_bps > 0;
-  if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV)) return PKV_ERR_INVALID;
+  if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV | PKV_DECODE_VECTOR)) return PKV_ERR_INVALID;
   // ---- shape and type checks
   if (!valid_dtype(kv_dtype) || !(out_dtype == kv_dtype || out_dtype == PKV_F32)) return PKV_ERR_INVALID;
   if (kv_fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale))) return PKV_ERR_INVALID;
@@ -381,13 +381,18 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
     path = 0;
   } else {
     if (group > 16) return PKV_ERR_UNSUPPORTED;
-    path = 1;   // MFMA for every group size (padded heads): measured 2 % faster than the vector path at G = 1
+    path = 1;   // MFMA for every group size (heads padded to 16)
+    if (flags & PKV_DECODE_VECTOR) {   // per-token dot products and shuffle reductions instead
+      if (kv_fp8 || group > 1) return PKV_ERR_UNSUPPORTED;
+      path = 0;
+    }
   }
   const int64_t max_blocks = (static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size;
   if (flat) {
     if (kv_fp8 || kv_dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;   // flat spans: 16-bit KV
     if (max_blocks > flat_bps || num_blocks % flat_bps) return PKV_ERR_INVALID;
     if (flags & PKV_DECODE_SHARED_KV) return PKV_ERR_UNSUPPORTED;    // spans are never shared
+    if (path != 1) return PKV_ERR_UNSUPPORTED;                        // spans decode on MFMA
   } else if (block_table_stride < max_blocks || block_table_stride < 0) {
     return PKV_ERR_INVALID;
   }

@@ -370,9 +370,11 @@ __device__ inline void vload(unsigned& d, const void* p) {
   else d = *static_cast<const unsigned*>(p);
 }
 // waits until at most N vector-memory operations are outstanding
+// (the memory clobber keeps every memory access of the source on its side of the wait: a read of
+// LDS that a global-to-LDS load fills must not be scheduled above the wait that retires that load)
 template <bool E, int N> __device__ inline void vm_wait() {
   static_assert(!E || (N >= 0 && N < 64), "vmcnt holds 6 bits");
-  if constexpr (E) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N));
+  if constexpr (E) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 // orders every later use of r after the preceding wait
 template <bool E, typename R> __device__ inline void tie(R& r) { if constexpr (E) asm volatile("" : "+v"(r)); }
@@ -680,6 +682,7 @@ __device__ inline typename Vec8<T>::type widen8(unsigned w0, unsigned w1) {
 template <typename T, int D, typename KV = T>
 struct MfmaMath {
   static constexpr int QH = 1;            // q fragment sets parked per unit
+  static constexpr bool kGroup = false;   // takes G from the kernel arguments
   static constexpr int NQ = D / 32;       // q vectors per lane: one per 32-wide MFMA k-step
   static constexpr bool kPrefetchQ = true;
   static constexpr bool kQuant = !std::is_same<KV, T>::value;
@@ -871,6 +874,7 @@ template <typename T, int D, int GM>
 struct VecMath {
   static constexpr int QH = GM;
   static constexpr bool kPrefetchQ = GM == 1;   // more heads: q is loaded at the unit switch
+  static constexpr bool kGroup = true;
   using Tile = Tile16<T, D>;
   static constexpr int NQ = Tile::NK;
   static constexpr int X = Kv<T>::X;
@@ -899,6 +903,11 @@ struct VecMath {
       load_q_head_lds<T, T, D>(a, u.s, u.kvh * a.group + (gi < a.group ? gi : 0), slot[gi]);
   }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
+    if constexpr (sizeof(T) == 4) compute_f32(R, q_lds, t0, ntok, scale_log2);
+    else compute_16(R, q_lds, t0, ntok, scale_log2);
+  }
+  // fp32 KV: the tile's keys and values are read once as floats for all heads
+  __device__ void compute_f32(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
     const bool partial = t0 + 16 > ntok;
     float kv[Tile::NK][X];
@@ -925,28 +934,66 @@ struct VecMath {
 #pragma unroll
         for (int e = 0; e < X; ++e) dot = fmaf(qv[e], kv[ks][e], dot);
       }
-      dot = sum_x32(sum_x16(dot));
-      float xs = dot * scale_log2;
-      if (partial && t0 + r16 >= ntok) xs = -INFINITY;
-      float mt = fmaxf(xs, xor_f(xs, 1));
-      mt = fmaxf(mt, xor_f(mt, 2));
-      mt = fmaxf(mt, xor_f(mt, 4));
-      mt = fmaxf(mt, xor_f(mt, 8));
-      const float m_new = fmaxf(m_run[gi], mt);
-      const float alpha = fast_exp2(m_run[gi] - m_new);
-      m_run[gi] = m_new;
-      const float p = fast_exp2(xs - m_new);    // weight of token t0 + r16
-      l_run[gi] = l_run[gi] * alpha + (g == 0 ? p : 0.f);
-      float pe[4];
+      head_update(gi, dot, partial, r16, g, t0, ntok, scale_log2, [&](int dt, float* v4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pe[i] = lane_fetch(p, 4 * g + i);
+        for (int i = 0; i < 4; ++i) v4[i] = vv[dt][i];
+      });
+    }
+  }
+  // 16-bit KV (one head): each stored vector is widened to fp32 where it is used, so that no more than
+  // one vector's floats are live at a time (widening the whole tile at once kept 64 more registers
+  // live, which 16-bit tiles cannot afford next to the tile buffers)
+  __device__ void compute_16(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
+    static_assert(GM == 1, "the 16-bit vector path takes one head per KV head");
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const bool partial = t0 + 16 > ntok;
+    float dot = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        float s4 = acc[gi][dt] * alpha;
+    for (int ks = 0; ks < Tile::NK; ++ks) {
+      float kv[X], qv[X];
+      unpack16<T>(R.kf[ks], kv);
+      unpack16<T>(q_lds[0][ks][threadIdx.x], qv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s4 = fmaf(pe[i], vv[dt][i], s4);
-        acc[gi][dt] = s4;
+      for (int e = 0; e < X; ++e) dot = fmaf(qv[e], kv[e], dot);
+    }
+    head_update(0, dot, partial, r16, g, t0, ntok, scale_log2, [&](int dt, float* v4) {
+      unpack4<T>(R.vf[dt], v4);
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * g + i >= ntok) v4[i] = 0.f;
       }
+    });
+  }
+  // head gi's share of a tile from the lane's partial dot product: the 4-lane reduction, the online
+  // softmax over the tile's 16 tokens and the value accumulation (values_of(dt, v4): the lane's 4
+  // tokens of value dim 16 dt + lane % 16, masked)
+  template <class Values>
+  __device__ void head_update(int gi, float dot, bool partial, int r16, int g, int t0, int ntok, float scale_log2,
+                              Values values_of) {
+    dot = sum_x32(sum_x16(dot));
+    float xs = dot * scale_log2;
+    if (partial && t0 + r16 >= ntok) xs = -INFINITY;
+    float mt = fmaxf(xs, xor_f(xs, 1));
+    mt = fmaxf(mt, xor_f(mt, 2));
+    mt = fmaxf(mt, xor_f(mt, 4));
+    mt = fmaxf(mt, xor_f(mt, 8));
+    const float m_new = fmaxf(m_run[gi], mt);
+    const float alpha = fast_exp2(m_run[gi] - m_new);
+    m_run[gi] = m_new;
+    const float p = fast_exp2(xs - m_new);    // weight of token t0 + r16
+    l_run[gi] = l_run[gi] * alpha + (g == 0 ? p : 0.f);
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = lane_fetch(p, 4 * g + i);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      float vv[4];
+      values_of(dt, vv);
+      float s4 = acc[gi][dt] * alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4 = fmaf(pe[i], vv[i], s4);
+      acc[gi][dt] = s4;
     }
   }
   __device__ void finish(const DecodeArgs& a, const Unit<T>& u) {
@@ -1031,6 +1078,8 @@ void decode_kernel(DecodeArgs a) {
   constexpr bool E = sizeof(Tile) <= 32 * 4;
   constexpr int LT = Tile::kLoads;   // every step issues exactly this many tile loads
   static_assert(!E || (NB - 1) * LT < 64, "vmcnt holds 6 bits");
+  // q straight into LDS needs the explicit waits: the compiler's own waits do not know of such a load
+  constexpr bool kQDma = Math::kPrefetchQ && E;
   constexpr int kClaimAhead = 4;   // take the next unit this many tiles before it is needed
   const int64_t chunk = static_cast<int64_t>(D) * Bsz;
   const int64_t blk_stride = chunk * a.n_kv_heads;
@@ -1122,7 +1171,7 @@ void decode_kernel(DecodeArgs a) {
         // the unit's q goes straight into its LDS slot, ahead of the unit's first tile loads: the
         // compute side reads the slot only after the wait that retires that tile (slot_i belongs to
         // a unit the compute side has finished)
-        if constexpr (Math::kPrefetchQ) Math::load_q_lds(a, ui, q_lds[slot_i]);
+        if constexpr (kQDma) Math::load_q_lds(a, ui, q_lds[slot_i]);
       }
     }
     const bool is_real = ti < ui.ntok;
@@ -1149,7 +1198,7 @@ void decode_kernel(DecodeArgs a) {
 
   Math mt;
   mt.reset();
-  if constexpr (!Math::kPrefetchQ) mt.group = a.group;
+  if constexpr (Math::kGroup) mt.group = a.group;
   const float scale_log2 = a.scale_log2;
 
   // Step `xi` of the unrolled loop: computes buffer xi (issued NB - 1 steps ago) and issues the next
@@ -1174,7 +1223,7 @@ void decode_kernel(DecodeArgs a) {
     fl &= ~kAhead;
     tc = 0;
     mt.reset();
-    if constexpr (!Math::kPrefetchQ) {
+    if constexpr (!kQDma) {
       Math::template load_q<false>(a, uc, qr);   // the compiler waits for these itself
       park_q(slot_c);
     }
@@ -1299,13 +1348,17 @@ const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8,
     return nullptr;
   }
   if (fp8) return nullptr;
-  // the vector path serves fp32 KV only (always streamed): 16-bit KV takes the MFMA path
+  // the vector path: fp32 KV (always streamed), and 16-bit KV with G = 1 when the caller asks for it
   if constexpr (sizeof(T) == 4) {
     if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>, true>(block_size);
     if (group == 2) return kernel_ptr_b<T, D, VecMath<T, D, 2>, true>(block_size);
     return kernel_ptr_b<T, D, VecMath<T, D, 4>, true>(block_size);
+  } else {
+    if (group == 1)
+      return nt ? kernel_ptr_b<T, D, VecMath<T, D, 1>, true>(block_size)
+                : kernel_ptr_b<T, D, VecMath<T, D, 1>, false>(block_size);
+    return nullptr;
   }
-  return nullptr;
 }
 
 template <typename T>

@@ -153,6 +153,7 @@ class DecodeBatch:
         self.slot_dev = torch.empty(self.S, dtype=torch.int64, device=dev)
         self.steps = 0
         self.load_policy = "auto"   # "auto", "streamed" or "cached": how decode reads the pools
+        self.vector = False         # one head per KV head on the per-token vector path (decode_only)
 
     STAGES = 8
     STAGE_EVENT_EVERY = 4
@@ -226,7 +227,7 @@ class DecodeBatch:
         c = self.cache
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
-                               shared_kv=self._keep_cached(), **c.scales)
+                               shared_kv=self._keep_cached(), vector=self.vector, **c.scales)
 
 
 class FlatKVCache:

@@ -100,7 +100,7 @@ class GpuState:
         torch.cuda.synchronize()
 
     def decode(self, out_dtype=None, partition_size=None, max_seq_len=None, q=None, workspace=None,
-               shared_kv=False, scales=None):
+               shared_kv=False, scales=None, vector=False):
         w = self.w
         odt = TORCH_DTYPE[w.dtype] if out_dtype is None else out_dtype
         q = self.q if q is None else q
@@ -108,7 +108,7 @@ class GpuState:
         self.pkv.paged_attention_decode(out, q, self.k_pool, self.v_pool, self.tables, self.seq_lens,
                                         w.scale, w.max_seq_len if max_seq_len is None else max_seq_len,
                                         w.partition_size if partition_size is None else partition_size,
-                                        workspace=workspace, shared_kv=shared_kv,
+                                        workspace=workspace, shared_kv=shared_kv, vector=vector,
                                         **(self.scales if scales is None else scales))
         torch.cuda.synchronize()
         return out

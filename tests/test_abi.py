@@ -103,7 +103,9 @@ def test_scatter_and_append_reject_bad_arguments():
     assert g(16, 0, 16, 8, 16, 16, None) == pkv.PKV_OK
     d = lib.pkv_paged_attention_decode_ex
     assert d(16, F16, 16, 16, 16, 16, 8, 16, 1, 8, 2, 128, 16, 100, 0.1, 128, 512, 256, 1 << 30, F16,
-             2, None) == pkv.PKV_ERR_INVALID                                              # unknown flag
+             4, None) == pkv.PKV_ERR_INVALID                                              # unknown flag
+    assert d(16, F16, 16, 16, 16, 16, 8, 16, 1, 8, 2, 128, 16, 100, 0.1, 128, 512, 256, 1 << 30, F16,
+             2, None) == pkv.PKV_ERR_UNSUPPORTED                        # the vector path takes G = 1 only
     c = lib.pkv_copy_blocks
     assert c(16, 16, 16, -1, 10, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID            # n_pairs < 0
     assert c(16, 16, 16, 1, 0, 2, 128, 16, F16, None) == pkv.PKV_ERR_INVALID              # no pool
@@ -156,7 +158,8 @@ def test_fp8_entries_reject_bad_arguments_before_launch():
     for bad in (0.0, -2.0, float("inf"), float("nan")):
         assert dec(kscale=bad) == pkv.PKV_ERR_INVALID
         assert dec(vscale=bad) == pkv.PKV_ERR_INVALID
-    assert dec(flags=2) == pkv.PKV_ERR_INVALID
+    assert dec(flags=4) == pkv.PKV_ERR_INVALID
+    assert dec(flags=2) == pkv.PKV_ERR_UNSUPPORTED      # the vector path reads 16-bit pools only
     assert dec(Hq=34, Hk=2) == pkv.PKV_ERR_UNSUPPORTED                  # group 17
     assert dec(D=96) == pkv.PKV_ERR_UNSUPPORTED
     assert dec(q=None) == pkv.PKV_ERR_INVALID

@@ -121,6 +121,29 @@ def test_heads_dims_blocks_sweep(dtype, G, D, B):
     assert torch.equal(out[0].cpu(), exp)
 
 
+@pytest.mark.parametrize("dtype,D,B", [("f16", 128, 16), ("bf16", 128, 8), ("f16", 64, 32), ("bf16", 64, 16)])
+def test_vector_path_for_one_head_per_kv_head(dtype, D, B):
+    """16-bit KV with G = 1 on the per-token vector path (fp32 dot products, cross-lane reductions)
+    instead of MFMA with the head padded to 16: within the tolerance of the oracle, streamed and
+    cacheable, and only for G = 1."""
+    lens = [1, 15, 16, 17, 33, 100, 511, 513, 1000]
+    w = wl.custom(seed=300 + D + B, lens=lens, n_q_heads=4, n_kv_heads=4, head_dim=D, block_size=B, dtype=dtype,
+                  partition_size=128)
+    st = GpuState(w)
+    ref = oracle_all(w)
+    for shared in (False, True):
+        out = st.decode(out_dtype=torch.float32, vector=True, shared_kv=shared)
+        err, row = max_abs_err_rows(out, ref)
+        log(f"vector path {dtype} D={D} B={B} shared={shared}: max abs err {err:.3e} (row {row})")
+        assert err <= TOL[dtype], err
+    K, V = wl.logical_kv(w, 0)                       # length 1: exactly the value row
+    assert torch.equal(out[0].cpu(), V[0].float())
+    w8 = wl.custom(seed=5, lens=[40], n_q_heads=8, n_kv_heads=4, head_dim=D, block_size=B, dtype=dtype)
+    st8 = GpuState(w8)
+    with pytest.raises(pkv.PKVError):
+        st8.decode(vector=True)                      # G = 2: MFMA only
+
+
 def test_empty_rows_are_zero():
     w = wl.custom(seed=5, lens=[40, 1, 70], n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16, dtype="bf16")
     st = GpuState(w)
