@@ -180,7 +180,8 @@ int pkv_append_slots(const int64_t* slot_mapping, int32_t num_seqs, int32_t* blo
  *   block_tables   device int32 [num_seqs][block_table_stride]; only the first
  *                  ceil(L/B) entries of a row are read; an entry outside
  *                  [0, num_blocks) is clamped into it (no fault; the row's result is
- *                  then meaningless)
+ *                  then meaningless: pkv_check_block_tables / pkv_validate_block_tables
+ *                  report such entries)
  *   seq_lens       device int32 [num_seqs]; a length above max_seq_len is treated as
  *                  max_seq_len
  *   max_seq_len    host bound on seq_lens, sizes the workspace
@@ -224,6 +225,29 @@ int pkv_paged_attention_decode_ex(void* out, int out_dtype, const void* q, const
                                   int32_t num_blocks, float scale, int32_t max_seq_len, int32_t partition_size,
                                   void* workspace, size_t workspace_bytes, int kv_dtype, uint32_t flags,
                                   void* stream);
+
+/* ---- finding a bad block table -------------------------------------------------------------------
+ * Decode reads, for row s, the block ids block_tables[s * stride + i], i < ceil(L / B), and an id
+ * outside [0, num_blocks) is clamped into the pool so that no access faults: the row's result is then
+ * meaningless and nothing reports it ("PagedAttention -- Math + Memory Model", section "PagedAttention:
+ * blocks and the block table": each of a sequence's logical blocks maps to a physical block of the
+ * pool).  These two calls report such entries instead; L is seq_lens[s] clamped to [0, max_seq_len] as
+ * decode clamps it, and block_table_stride must hold ceil(max_seq_len / B) entries.
+ *
+ * pkv_validate_block_tables: host arrays, checked on the CPU.  PKV_OK if every read entry is in the
+ * pool, else PKV_ERR_INVALID with *bad_entries = the number of out-of-pool entries and *first_bad_row =
+ * the first row holding one (-1 if none; both outputs nullable).
+ *
+ * pkv_check_block_tables: device arrays, checked by a kernel on `stream` (no allocation, no memset, so
+ * it may be captured in a graph).  It writes result[0] = the number of out-of-pool entries and
+ * result[1] = the first row holding one (INT32_MAX if none) to the caller's device int32 [2]; the
+ * caller reads them after the stream reaches that point.  Nothing traps on the GPU. */
+int pkv_validate_block_tables(const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              int64_t* bad_entries, int32_t* first_bad_row);
+int pkv_check_block_tables(const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                           int32_t num_seqs, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                           int32_t* result, void* stream);
 
 /* ---- decode attention without allocation --------------------------------------------------------
  * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,

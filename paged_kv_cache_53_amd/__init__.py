@@ -31,7 +31,7 @@ __all__ = [
     "workspace_size", "key_pool_shape", "value_pool_shape", "pool_bytes", "dtype_code",
     "timing_enable", "timing_select", "timing_collect", "lib", "copy_blocks", "SpanPool",
     "reshape_and_cache_spans", "paged_attention_decode_flat", "swap_blocks", "decode_step",
-    "paged_attention_decode_noalloc", "read_probe",
+    "paged_attention_decode_noalloc", "read_probe", "validate_block_tables", "check_block_tables",
 ]
 
 
@@ -530,3 +530,39 @@ def read_probe(buf, waves_per_cu: int, loads_per_batch: int, nontemporal: bool =
                                 int(loads_per_batch), mode, _ptr(sink), C.byref(n), _stream(stream)),
            "pkv_read_probe")
     return int(n.value)
+
+
+def validate_block_tables(tables, seq_lens, block_size: int, num_blocks: int, max_seq_len: int):
+    """Host check of the entries decode would read (pkv_validate_block_tables): returns (number of
+    out-of-pool entries, first row holding one or -1).  tables: int32 [S, stride], seq_lens: int32 [S]
+    (numpy arrays or CPU tensors)."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tables, dtype=np.int32))
+    L = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if t.ndim != 2 or L.shape != (t.shape[0],):
+        raise ValueError("tables must be [S, stride] and seq_lens [S]")
+    bad, first = C.c_int64(0), C.c_int32(-1)
+    st = lib().pkv_validate_block_tables(t.ctypes.data_as(C.POINTER(C.c_int32)), t.shape[1],
+                                         L.ctypes.data_as(C.POINTER(C.c_int32)), t.shape[0], int(block_size),
+                                         int(num_blocks), int(max_seq_len), C.byref(bad), C.byref(first))
+    if st not in (PKV_OK, PKV_ERR_INVALID):
+        _check(st, "pkv_validate_block_tables")
+    if st == PKV_ERR_INVALID and bad.value == 0:
+        raise PKVError(st, "pkv_validate_block_tables")
+    return int(bad.value), int(first.value)
+
+
+def check_block_tables(tables, seq_lens, block_size: int, num_blocks: int, max_seq_len: int, result=None,
+                       stream=None):
+    """Device check of the entries decode would read (pkv_check_block_tables), queued on the stream:
+    returns the device int32 [2] tensor {out-of-pool entries, first row holding one (INT32_MAX if
+    none)}; read it after the stream has run the check."""
+    import torch
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=tables.device)
+    if tables.dim() != 2 or tables.stride(1) != 1 or tuple(seq_lens.shape) != (tables.shape[0],):
+        raise ValueError("tables must be [S, stride] with unit column stride and seq_lens [S]")
+    _check(lib().pkv_check_block_tables(_ptr(tables), tables.stride(0), _ptr(seq_lens), tables.shape[0],
+                                        int(block_size), int(num_blocks), int(max_seq_len), _ptr(result),
+                                        _stream(stream)), "pkv_check_block_tables")
+    return result

@@ -97,6 +97,8 @@ SIGNATURES = {
     "pkv_timing_collect": (C.c_int, [C.POINTER(pkv_kernel_time), I32, PI32]),
     "pkv_timing_select": (C.c_int, [C.c_uint32]),
     "pkv_read_probe": (C.c_int, [P, SZ, I32, I32, C.c_int, P, C.POINTER(SZ), P]),
+    "pkv_validate_block_tables": (C.c_int, [PI32, I32, PI32, I32, I32, I32, I32, PI64, PI32]),
+    "pkv_check_block_tables": (C.c_int, [P, I32, P, I32, I32, I32, I32, P, P]),
 }
 
 _lib = None

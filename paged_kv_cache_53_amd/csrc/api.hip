@@ -628,6 +628,46 @@ int pkv_decode_step(const pkv_decode_step_args* p, void* stream) {
   return decode_launch(L, false, st);
 }
 
+int pkv_check_block_tables(const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                           int32_t num_seqs, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                           int32_t* result, void* stream) {
+  if (num_seqs < 0 || block_table_stride <= 0 || block_size <= 0 || num_blocks <= 0 || max_seq_len < 0 || !result ||
+      !aligned(result, 4))
+    return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !aligned(block_tables, 4) || !aligned(seq_lens, 4)))
+    return PKV_ERR_INVALID;
+  if ((static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size > block_table_stride) return PKV_ERR_INVALID;
+  return launch_check_tables(block_tables, block_table_stride, seq_lens, num_seqs, block_size, num_blocks,
+                             max_seq_len, result, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+int pkv_validate_block_tables(const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              int64_t* bad_entries, int32_t* first_bad_row) {
+  if (num_seqs < 0 || block_table_stride <= 0 || block_size <= 0 || num_blocks <= 0 || max_seq_len < 0)
+    return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!block_tables || !seq_lens)) return PKV_ERR_INVALID;
+  if ((static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size > block_table_stride) return PKV_ERR_INVALID;
+  int64_t bad = 0;
+  int32_t first = -1;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = seq_lens[s] < 0 ? 0 : (seq_lens[s] > max_seq_len ? max_seq_len : seq_lens[s]);
+    const int32_t nb = (L + block_size - 1) / block_size;
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t id = block_tables[static_cast<int64_t>(s) * block_table_stride + i];
+      if (id < 0 || id >= num_blocks) {
+        ++bad;
+        if (first < 0) first = s;
+      }
+    }
+  }
+  if (bad_entries) *bad_entries = bad;
+  if (first_bad_row) *first_bad_row = first;
+  return bad ? PKV_ERR_INVALID : PKV_OK;
+}
+
 int pkv_timing_enable(int enable) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

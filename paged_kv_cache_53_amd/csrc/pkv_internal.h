@@ -92,6 +92,10 @@ hipError_t launch_append_slots(const int64_t* slot_mapping, int32_t num_seqs, in
                                int32_t stride, int32_t* seq_lens, int32_t block_size,
                                hipStream_t stream);
 hipError_t launch_decode_plan(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Counts out-of-pool block-table entries among each row's first ceil(L / B) (result: {count, first row}).
+hipError_t launch_check_tables(const int32_t* tables, int32_t stride, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len, int32_t* result,
+                               hipStream_t stream);
 // The fused step's first kernel: append, scatter (sc.num_tokens == a.num_seqs tokens, rows of
 // dtype; kv_fp8: quantised pools) and plan.  head_dim must be 64 or 128.
 hipError_t launch_step_prologue(const DecodeArgs& a, const ScatterArgs& sc, const StepArgs& st, int dtype,

@@ -79,7 +79,45 @@ __global__ __launch_bounds__(256) void move_blocks_kernel(const void* src_k, con
     d[i] = s[i];
 }
 
+// Counts block-table entries outside [0, num_blocks) among each row's first ceil(L / B) entries
+// (L: the row's length, clamped to [0, max_seq_len] as decode clamps it).  One workgroup per row;
+// result[0] += bad entries, result[1] = min(result[1], first row with one).  Plain vector atomics.
+__global__ __launch_bounds__(256) void check_tables_kernel(const int32_t* __restrict__ tables, int32_t stride,
+                                                           const int32_t* __restrict__ seq_lens, int32_t block_size,
+                                                           int32_t num_blocks, int32_t max_seq_len,
+                                                           int32_t* result) {
+  const int s = blockIdx.x;
+  int L = seq_lens[s];
+  L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+  const int nb = (L + block_size - 1) / block_size;
+  int bad = 0;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    const int id = tables[static_cast<int64_t>(s) * stride + i];
+    bad += (id < 0 || id >= num_blocks) ? 1 : 0;
+  }
+  if (bad) {
+    atomicAdd(&result[0], bad);
+    atomicMin(&result[1], s);
+  }
+}
+
+// result = {0, INT32_MAX}: a kernel, not a memset, so the check may sit in a captured graph
+__global__ void check_tables_reset_kernel(int32_t* result) {
+  result[0] = 0;
+  result[1] = 0x7FFFFFFF;
+}
+
 }  // namespace
+
+hipError_t launch_check_tables(const int32_t* tables, int32_t stride, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len, int32_t* result,
+                               hipStream_t st) {
+  check_tables_reset_kernel<<<1, 1, 0, st>>>(result);
+  if (num_seqs > 0)
+    check_tables_kernel<<<num_seqs, 256, 0, st>>>(tables, stride, seq_lens, block_size, num_blocks, max_seq_len,
+                                                  result);
+  return hipGetLastError();
+}
 
 hipError_t launch_move_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
                               int32_t dst_blocks, const int32_t* pairs, int32_t n_pairs, int64_t block_bytes,

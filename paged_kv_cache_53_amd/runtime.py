@@ -33,9 +33,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (Allocator, SpanPool, append_slots, copy_blocks, decode_step, key_pool_shape, paged_attention_decode,
-               paged_attention_decode_flat, reshape_and_cache, reshape_and_cache_spans, swap_blocks,
-               value_pool_shape, workspace_size)
+from . import (PKV_ERR_INVALID, Allocator, PKVError, SpanPool, append_slots, check_block_tables, copy_blocks,
+               decode_step, key_pool_shape, paged_attention_decode, paged_attention_decode_flat, reshape_and_cache,
+               reshape_and_cache_spans, swap_blocks, value_pool_shape, workspace_size)
 
 
 class PagedKVCache:
@@ -154,6 +154,8 @@ class DecodeBatch:
         self.steps = 0
         self.load_policy = "auto"   # "auto", "streamed" or "cached": how decode reads the pools
         self.vector = False         # one head per KV head on the per-token vector path (decode_only)
+        self.check_tables = False   # debug mode: check the device tables before each decode (synchronises)
+        self._check_result = torch.empty(2, dtype=torch.int32, device=dev)
 
     STAGES = 8
     STAGE_EVENT_EVERY = 4
@@ -183,6 +185,16 @@ class DecodeBatch:
                 del self.step_events[k]
         return n % self.STAGES
 
+    def _verify_tables(self) -> None:
+        """Debug mode: every table entry the next decode reads must name a block of the pool (decode
+        clamps an out-of-pool id, which would give a wrong row silently)."""
+        c = self.cache
+        r = check_block_tables(self.tables, self.seq_lens, c.block_size, c.num_blocks, self.max_seq_len,
+                               result=self._check_result)
+        bad, first = (int(x) for x in r.cpu())
+        if bad:
+            raise PKVError(PKV_ERR_INVALID, f"block tables hold {bad} out-of-pool entries (first in batch row {first})")
+
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out: torch.Tensor,
              fused: bool = True) -> None:
         """One decode step for every row: append the new token, write its K/V, attend over all tokens.
@@ -192,6 +204,8 @@ class DecodeBatch:
         paged_attention_decode run as separate calls.  The results are the same."""
         if int(self.host_lens.max(initial=0)) + 1 > self.max_seq_len:
             raise ValueError("decode step would exceed max_seq_len")
+        if self.check_tables:
+            self._verify_tables()
         i = self._stage_for(self.steps)
         _, pairs = self.cache.allocator.alloc_batch(self.seq_ids, 1, slots_out=self.slot_stage_np[i])
         self.host_lens += 1
@@ -224,6 +238,8 @@ class DecodeBatch:
 
     def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
         """Attention over the current tokens without appending (no host work, no scatter)."""
+        if self.check_tables:
+            self._verify_tables()
         c = self.cache
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,

@@ -285,3 +285,22 @@ def test_noalloc_decode_rejects_calls_beyond_its_static_scratch():
                                                32768, 512, F16, 0, None)
     assert r == pkv.PKV_ERR_SCRATCH
     assert "static scratch" in lib.pkv_status_string(pkv.PKV_ERR_SCRATCH).decode()
+
+
+def test_host_table_validator_reports_out_of_pool_entries():
+    import numpy as np
+    B, N = 16, 100
+    tables = np.array([[3, 4, 5, 0], [7, 99, -1, 0], [1, 2, 150, 151]], dtype=np.int32)
+    lens = np.array([40, 17, 33], dtype=np.int32)   # reads 3, 2 and 3 entries
+    # row 1 reads 7 and 99 (fine); row 2 reads 1, 2 and 150 (out of the pool); -1 and 151 are never read
+    assert pkv.validate_block_tables(tables, lens, B, N, 64) == (1, 2)
+    lens2 = np.array([40, 33, 33], dtype=np.int32)   # now row 1 also reads its -1
+    assert pkv.validate_block_tables(tables, lens2, B, N, 64) == (2, 1)
+    # lengths above max_seq_len are clamped, as decode clamps them: row 2 then reads two entries only
+    assert pkv.validate_block_tables(tables, lens, B, N, 32) == (0, -1)
+    assert pkv.validate_block_tables(tables[:, :3], lens, B, N, 48) == (1, 2)
+    with pytest.raises(pkv.PKVError):
+        pkv.validate_block_tables(tables[:, :2], lens, B, N, 64)    # the stride holds fewer than 64 tokens
+    lib = pkv.lib()
+    assert lib.pkv_check_block_tables(16, 4, 16, 3, B, N, 64, None, None) == pkv.PKV_ERR_INVALID   # no result
+    assert lib.pkv_check_block_tables(16, 2, 16, 3, B, N, 64, 16, None) == pkv.PKV_ERR_INVALID     # stride
