@@ -328,15 +328,29 @@ def check_kernel(body: List[str]) -> List[str]:
     return sorted(reports)
 
 
-def check_file(path: str, substring: str = "decode_kernel") -> Dict[str, List[str]]:
+def _check_body(body: List[str]) -> List[str]:
+    return check_kernel(body)
+
+
+def check_file(path: str, substring: str = "decode_kernel", workers: Optional[int] = None) -> Dict[str, List[str]]:
+    """Checks every kernel whose name contains `substring`, the kernels spread over worker processes."""
+    import os
+    from concurrent.futures import ProcessPoolExecutor
     s = open(path).read()
     names = sorted(set(re.findall(r"^(\S*" + re.escape(substring) + r"\S*):\s*(?:;.*)?$", s, re.M)))
-    out = {}
+    bodies = []
     for name in names:
         a = s.index(name + ":")
         b = s.index(".Lfunc_end", a)
-        out[name] = check_kernel(s[a:b].splitlines()[1:])
-    return out
+        bodies.append(s[a:b].splitlines()[1:])
+    n = workers or min(16, len(os.sched_getaffinity(0)))
+    if n <= 1 or len(bodies) <= 1:
+        return {name: check_kernel(body) for name, body in zip(names, bodies)}
+    # largest bodies first, so that the long checks start early
+    order = sorted(range(len(bodies)), key=lambda i: -len(bodies[i]))
+    with ProcessPoolExecutor(n) as ex:
+        results = dict(zip(order, ex.map(_check_body, [bodies[i] for i in order])))
+    return {names[i]: results[i] for i in range(len(names))}
 
 
 def main(argv: List[str]) -> int:
