@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--decode-only", action="store_true", help="time the decode call alone (no append/scatter)")
     p.add_argument("--reps", type=int, default=20,
                    help="separately collected launches for the decode kernel's median / p10 / p90")
-    p.add_argument("--load-policy", default="auto", choices=["auto", "streamed", "cached"],
+    p.add_argument("--load-policy", default="auto", choices=["auto", "streamed", "cached", "prefix"],
                    help="how decode reads the pools (auto: the runtime's rule)")
     p.add_argument("--flush", action="store_true",
                    help="also time --reps launches after a 1 GiB write and --reps after a 1 GiB read "
@@ -91,6 +91,8 @@ def parse():
                    help="time the copy-on-write block copy kernel alone (4096 random block pairs)")
     p.add_argument("--swap", action="store_true",
                    help="time block moves between the pool and pinned host swap space (4096 blocks each way)")
+    p.add_argument("--shared-prefix-tokens", type=int, default=None,
+                   help="with --load-policy prefix: the prefix read cacheable (default: the batch's shared prefix)")
     p.add_argument("--math", default="mfma", choices=["mfma", "vector"],
                    help="with --decode-only: vector = the per-token vector path (16-bit KV, one head per KV head)")
     p.add_argument("--read-ceiling", action="store_true",
@@ -159,6 +161,14 @@ def kv_bytes(w, lens, table=True):
     return kv, tb
 
 
+def load_description(batch):
+    """How the decode batch reads the pools (the runtime's load policy in effect)."""
+    args = batch._load_args()
+    if args.get("shared_prefix_tokens"):
+        return f"first {args['shared_prefix_tokens']} tokens of each row cacheable, the rest streamed"
+    return "cached" if args.get("shared_kv") else "streamed"
+
+
 def duplicate_tokens(tables, lens, block_size):
     """Tokens the rows of a batch read from blocks that another row of the batch also reads, beyond the
     first reading: every physical block's valid tokens count once towards the unique bytes HBM must
@@ -187,7 +197,7 @@ def percentiles_us(ms_values):
 
 
 def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True, reps=20,
-               flush=False, load_policy="auto", math="mfma"):
+               flush=False, load_policy="auto", math="mfma", shared_prefix_tokens=None):
     import numpy as np
     import torch
 
@@ -198,6 +208,8 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
     cache, batch = build_batch(w, extra_tokens=extra, layout=layout, chunk_bytes=chunk_bytes)
     if load_policy != "auto":
         batch.load_policy = load_policy
+    if shared_prefix_tokens is not None:
+        batch.shared_prefix = shared_prefix_tokens
     if math == "vector":
         if not decode_only or layout != "paged":
             raise SystemExit("--math vector times the paged decode call alone (--decode-only)")
@@ -290,7 +302,7 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
     return {"total_s": total_s, "kv_bytes": kvb, "table_bytes": tb, "kernels": kernels, "steps": steps,
             "kv_bytes_unique": kvb - dup * per_token * steps, "duplicate_tokens": dup,
             "lens0": lens0, "decode_timed": decode_timed, "diag_steps": diag,
-            "decode_loads": ("cached" if batch._keep_cached() else "streamed") if layout == "paged" else "streamed",
+            "decode_loads": load_description(batch) if layout == "paged" else "streamed",
             "decode_launch_us": percentiles_us(warm) if warm else None,
             "decode_launch_us_cold": cold or None}
 
@@ -639,7 +651,7 @@ def main():
     w = make_workload(args)
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
                      chunk_bytes=args.chunk_bytes, fused=not args.unfused, reps=args.reps, flush=args.flush,
-                     load_policy=args.load_policy, math=args.math)
+                     load_policy=args.load_policy, math=args.math, shared_prefix_tokens=args.shared_prefix_tokens)
     total_s = res["total_s"]
     gbps = (res["kv_bytes_unique"] + res["table_bytes"]) / total_s / 1e9
     gbps_logical = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9

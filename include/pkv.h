@@ -76,7 +76,8 @@ enum {
 /* Text for a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
 
-/* Library ABI version, bumped on any incompatible change. */
+/* Library ABI version, bumped on any incompatible change (2: pkv_decode_step_args gained
+ * shared_prefix_tokens). */
 int pkv_version(void);
 
 /* Bytes of ONE pool (key or value) for the given shape and pool element type (PKV_FP8_E4M3
@@ -289,6 +290,52 @@ int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q, 
 int pkv_read_probe(const void* buf, size_t bytes, int32_t waves_per_cu, int32_t loads_per_batch, int mode,
                    uint32_t* sink, size_t* bytes_read, void* stream);
 
+/* ---- decode attention: every option in one call ------------------------------------------------
+ * The decode of pkv_paged_attention_decode_ex (16-bit or fp32 pools) or pkv_paged_attention_decode_fp8
+ * (kv_fp8 = 1: FP8 E4M3 pools under k_scale / v_scale, q of q_dtype), with one more choice of how the
+ * pools are read:
+ *   shared_prefix_tokens  0, or n > 0: the first n tokens of every row lie in blocks that other rows of
+ *                         the batch read too (a prompt the rows were forked from, "KV-cache paging in
+ *                         vLLM", section "What This Changes in Practice": the shared blocks are
+ *                         physically shared, not copied).  Tiles of 16-bit and FP8 pools that start
+ *                         before token n are read with cacheable loads, so the rows that re-read them
+ *                         hit L2 and the Infinity Cache, and every later tile is streamed with the
+ *                         non-temporal hint, so a row's private tokens neither evict the shared ones nor
+ *                         pay for the write-back of dirty lines they would evict.  The choice is made per
+ *                         tile, with no change to any result.  It overrides PKV_DECODE_SHARED_KV (which
+ *                         reads every tile cacheable); on the vector path it reads every tile cacheable;
+ *                         flat spans: PKV_ERR_UNSUPPORTED.
+ * Every other field means what the argument of that name means for the calls above. */
+typedef struct {
+  void* out;
+  int32_t out_dtype;
+  const void* q;
+  int32_t q_dtype;
+  const void* k_pool;
+  const void* v_pool;
+  int32_t kv_fp8;
+  float k_scale;
+  float v_scale;
+  const int32_t* block_tables;
+  int32_t block_table_stride;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  float scale;
+  int32_t max_seq_len;
+  int32_t partition_size;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+  int32_t shared_prefix_tokens;
+} pkv_decode_args;
+
+int pkv_paged_attention_decode_v2(const pkv_decode_args* args, void* stream);
+
 /* ---- quantised cache: FP8 E4M3 pools ------------------------------------------------
  * Quantising the cached keys and values is the memory lever the pages put after paging: an
  * 8-bit cache halves the bytes each sequence's attention reads ("Contiguous vs Paged KV Cache
@@ -388,6 +435,7 @@ typedef struct {
   uint32_t flags;
   void* workspace;
   size_t workspace_bytes;
+  int32_t shared_prefix_tokens;   /* as in pkv_decode_args (0: none) */
 } pkv_decode_step_args;
 
 int pkv_decode_step(const pkv_decode_step_args* args, void* stream);

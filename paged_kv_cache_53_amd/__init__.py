@@ -188,11 +188,13 @@ PKV_DECODE_VECTOR = 2
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int,
                            partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False,
-                           k_scale=None, v_scale=None, vector: bool = False) -> None:
+                           k_scale=None, v_scale=None, vector: bool = False, shared_prefix_tokens: int = 0) -> None:
     """out[s, h] = softmax attention of q[s, h] over the row's paged K/V (see include/pkv.h).
 
     shared_kv: some blocks are read by more than one row (forks, a shared prompt); keeps them
     cacheable instead of streaming them.  Results are the same either way.
+    shared_prefix_tokens: n > 0 reads tiles before token n of each row cacheable and streams the rest
+    (pkv_paged_attention_decode_v2); overrides shared_kv.
     vector: 16-bit KV with one query head per KV head on the per-token vector path instead of MFMA.
     FP8 pools (float8_e4m3fn / uint8): attention over k_scale * value(code) and
     v_scale * value(code), with q in bf16 or f16."""
@@ -207,6 +209,21 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     flags = (PKV_DECODE_SHARED_KV if shared_kv else 0) | (PKV_DECODE_VECTOR if vector else 0)
+    if shared_prefix_tokens:
+        fp8 = _is_fp8_pool(k_pool)
+        if fp8 and (k_scale is None or v_scale is None):
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        args = _lib.pkv_decode_args(
+            out=_ptr(out), out_dtype=dtype_code(out), q=_ptr(q), q_dtype=dtype_code(q), k_pool=_ptr(k_pool),
+            v_pool=_ptr(v_pool), kv_fp8=1 if fp8 else 0, k_scale=float(k_scale) if fp8 else 1.0,
+            v_scale=float(v_scale) if fp8 else 1.0, block_tables=_ptr(block_tables),
+            block_table_stride=block_tables.stride(0), seq_lens=_ptr(seq_lens), num_seqs=S, n_q_heads=Hq,
+            n_kv_heads=Hk, head_dim=D, block_size=B, num_blocks=N, scale=float(scale), max_seq_len=int(max_seq_len),
+            partition_size=int(partition_size), workspace=_ptr(workspace),
+            workspace_bytes=workspace.numel() * workspace.element_size(), flags=flags,
+            shared_prefix_tokens=int(shared_prefix_tokens))
+        _check(lib().pkv_paged_attention_decode_v2(C.byref(args), _stream(stream)), "pkv_paged_attention_decode_v2")
+        return
     if _is_fp8_pool(k_pool):
         if k_scale is None or v_scale is None:
             raise ValueError("an FP8 cache needs k_scale and v_scale")
@@ -251,7 +268,7 @@ def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_len
 
 def decode_step(out, q, k, v, slot_mapping, k_pool, v_pool, block_tables, seq_lens, scale: float,
                 max_seq_len: int, partition_size: int = 512, workspace=None, stream=None, shared_kv: bool = False,
-                k_scale=None, v_scale=None) -> None:
+                k_scale=None, v_scale=None, shared_prefix_tokens: int = 0) -> None:
     """One decode step: append_slots, reshape_and_cache and paged_attention_decode with the same
     results, in fewer launches (pkv_decode_step).  Row s appends token s of k / v ([S, Hk, D], token
     rows may be strided) at slot_mapping[s]; slot_mapping is int64 [S] on the device or in pinned
@@ -290,7 +307,8 @@ def decode_step(out, q, k, v, slot_mapping, k_pool, v_pool, block_tables, seq_le
         num_seqs=S, n_q_heads=Hq, n_kv_heads=Hk, head_dim=D, block_size=B, out=_ptr(out),
         out_dtype=dtype_code(out), dtype=dtype_code(q), q=_ptr(q), scale=float(scale), max_seq_len=int(max_seq_len),
         partition_size=int(partition_size), flags=PKV_DECODE_SHARED_KV if shared_kv else 0,
-        workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size())
+        workspace=_ptr(workspace), workspace_bytes=workspace.numel() * workspace.element_size(),
+        shared_prefix_tokens=int(shared_prefix_tokens))
     _check(lib().pkv_decode_step(C.byref(a), _stream(stream)), "pkv_decode_step")
 
 

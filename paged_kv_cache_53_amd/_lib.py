@@ -36,7 +36,19 @@ class pkv_decode_step_args(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
                 ("out", C.c_void_p), ("out_dtype", C.c_int32), ("dtype", C.c_int32), ("q", C.c_void_p),
                 ("scale", C.c_float), ("max_seq_len", C.c_int32), ("partition_size", C.c_int32),
-                ("flags", C.c_uint32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("flags", C.c_uint32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("shared_prefix_tokens", C.c_int32)]
+
+
+class pkv_decode_args(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("out_dtype", C.c_int32), ("q", C.c_void_p), ("q_dtype", C.c_int32),
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("kv_fp8", C.c_int32), ("k_scale", C.c_float),
+                ("v_scale", C.c_float), ("block_tables", C.c_void_p), ("block_table_stride", C.c_int32),
+                ("seq_lens", C.c_void_p), ("num_seqs", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
+                ("num_blocks", C.c_int32), ("scale", C.c_float), ("max_seq_len", C.c_int32),
+                ("partition_size", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("flags", C.c_uint32), ("shared_prefix_tokens", C.c_int32)]
 
 
 class pkv_kernel_time(C.Structure):
@@ -70,6 +82,7 @@ SIGNATURES = {
     "pkv_paged_attention_decode_flat": (C.c_int, [P, C.c_int, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                                   C.c_float, I32, I32, P, SZ, C.c_int, C.c_uint32, P]),
     "pkv_decode_step": (C.c_int, [C.POINTER(pkv_decode_step_args), P]),
+    "pkv_paged_attention_decode_v2": (C.c_int, [C.POINTER(pkv_decode_args), P]),
     "pkv_span_pool_create": (C.c_int, [I32, I32, I32, I32, I32, C.c_int, SZ, C.POINTER(P)]),
     "pkv_span_pool_destroy": (None, [P]),
     "pkv_span_reserve": (C.c_int, [P, I32, I32]),

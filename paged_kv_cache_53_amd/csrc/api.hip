@@ -74,15 +74,15 @@ std::mutex cap_mu;
 std::unordered_map<int64_t, int32_t> cap_cache;
 
 hipError_t grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group, int block_size,
-                    bool nt, int32_t* cap) {
+                    int pol, int32_t* cap) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   // one entry per kernel variant: the vector path has one variant per group width (1, 2, 3-4),
-  // the MFMA path one per storage type and one for flat spans, each for both cache policies
+  // the MFMA path one per storage type and one for flat spans, each for every load policy
   const int variant = path == 1 ? (flat ? 5 : kv_fp8 ? 4 : 3) : (group == 1 ? 0 : group == 2 ? 1 : 2);
   const int64_t key = (((((static_cast<int64_t>(dev) * 4 + dtype) * 512 + head_dim) * 8 + variant) * 64) +
-                       block_size) * 2 + (nt ? 1 : 0);
+                       block_size) * 4 + pol;
   {
     std::lock_guard<std::mutex> g(cap_mu);
     auto it = cap_cache.find(key);
@@ -91,7 +91,7 @@ hipError_t grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, i
       return hipSuccess;
     }
   }
-  e = decode_main_grid_cap(dtype, kv_fp8, flat, head_dim, path, group, block_size, nt, cap);
+  e = decode_main_grid_cap(dtype, kv_fp8, flat, head_dim, path, group, block_size, pol, cap);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> g(cap_mu);
   cap_cache[key] = *cap;
@@ -165,7 +165,7 @@ const char* pkv_status_string(int status) {
   }
 }
 
-int pkv_version(void) { return 1; }
+int pkv_version(void) { return 2; }
 
 size_t pkv_pool_bytes(int32_t num_blocks, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
                       int dtype) {
@@ -344,8 +344,8 @@ namespace {
 // A checked decode call, ready to launch.
 struct DecodeLaunch {
   DecodeArgs a;
-  int kv_dtype, head_dim, path;
-  bool kv_fp8, nt;
+  int kv_dtype, head_dim, path, pol;
+  bool kv_fp8;
   int32_t grid;
   bool empty;   // no rows: nothing to launch
 };
@@ -359,8 +359,9 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
                    int32_t block_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t n_q_heads,
                    int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                    int32_t max_seq_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   uint32_t flags, int32_t flat_bps = 0) {
+                   uint32_t flags, int32_t flat_bps = 0, int32_t shared_prefix_tokens = 0) {
   L->empty = false;
+  if (shared_prefix_tokens < 0) return PKV_ERR_INVALID;
   const int kv_dtype = q_dtype;   // the compute type of the kernels
   const bool flat = flat_bps > 0;
   if (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV | PKV_DECODE_VECTOR)) return PKV_ERR_INVALID;
@@ -442,15 +443,22 @@ int decode_prepare(DecodeLaunch* L, void* out, int out_dtype, const void* q, int
   a.v_scale = kv_fp8 ? v_scale : 1.f;
   a.flat_bps = flat ? flat_bps : 0;
 
-  const bool nt = (flags & PKV_DECODE_SHARED_KV) == 0;
+  // load policy: tiles in the rows' shared prefix cacheable and the rest streamed (MFMA path), else
+  // everything cacheable when blocks are shared, else everything streamed
+  int pol = (flags & PKV_DECODE_SHARED_KV) ? kLoadCached : kLoadStreamed;
+  if (shared_prefix_tokens > 0) {
+    if (flat) return PKV_ERR_UNSUPPORTED;   // spans are never shared
+    pol = path == 1 ? kLoadMixed : kLoadCached;
+  }
+  a.cache_tokens = pol == kLoadMixed ? shared_prefix_tokens : 0;
   int32_t cap = 0;
-  if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, nt, &cap) != hipSuccess) return PKV_ERR_HIP;
+  if (grid_cap(kv_dtype, kv_fp8, flat, head_dim, path, group, block_size, pol, &cap) != hipSuccess) return PKV_ERR_HIP;
   L->grid = static_cast<int32_t>(unit_bound < cap ? (unit_bound > 0 ? unit_bound : 1) : cap);
   L->kv_dtype = kv_dtype;
   L->head_dim = head_dim;
   L->path = path;
   L->kv_fp8 = kv_fp8;
-  L->nt = nt;
+  L->pol = pol;
   return PKV_OK;
 }
 
@@ -471,7 +479,7 @@ int decode_launch(const DecodeLaunch& L, bool plan, hipStream_t st, bool timed =
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   before(PKV_K_DECODE);
-  e = launch_decode_main(a, L.kv_dtype, L.kv_fp8, L.head_dim, L.path, L.nt, L.grid, st);
+  e = launch_decode_main(a, L.kv_dtype, L.kv_fp8, L.head_dim, L.path, L.pol, L.grid, st);
   after(PKV_K_DECODE);
   if (e != hipSuccess) return PKV_ERR_HIP;
   if (a.max_parts > 1) {
@@ -588,6 +596,18 @@ int pkv_paged_attention_decode_fp8(void* out, int out_dtype, const void* q, int 
                      num_blocks, scale, max_seq_len, partition_size, workspace, workspace_bytes, flags, stream);
 }
 
+int pkv_paged_attention_decode_v2(const pkv_decode_args* p, void* stream) {
+  if (!p || (p->kv_fp8 != 0 && p->kv_fp8 != 1)) return PKV_ERR_INVALID;
+  DecodeLaunch L;
+  const int r = decode_prepare(&L, p->out, p->out_dtype, p->q, p->q_dtype, p->k_pool, p->v_pool, p->kv_fp8 == 1,
+                               p->k_scale, p->v_scale, p->block_tables, p->block_table_stride, p->seq_lens,
+                               p->num_seqs, p->n_q_heads, p->n_kv_heads, p->head_dim, p->block_size, p->num_blocks,
+                               p->scale, p->max_seq_len, p->partition_size, p->workspace, p->workspace_bytes,
+                               p->flags, 0, p->shared_prefix_tokens);
+  if (r != PKV_OK) return r;
+  return decode_launch(L, true, static_cast<hipStream_t>(stream));
+}
+
 int pkv_decode_step(const pkv_decode_step_args* p, void* stream) {
   if (!p) return PKV_ERR_INVALID;
   // ---- the scatter's checks (one new token per row, rows of dtype)
@@ -611,7 +631,8 @@ int pkv_decode_step(const pkv_decode_step_args* p, void* stream) {
   const int r = decode_prepare(&L, p->out, p->out_dtype, p->q, dtype, p->k_pool, p->v_pool, fp8, p->k_scale,
                                p->v_scale, p->block_tables, p->block_table_stride, p->seq_lens, p->num_seqs,
                                p->n_q_heads, p->n_kv_heads, p->head_dim, p->block_size, p->num_blocks, p->scale,
-                               p->max_seq_len, p->partition_size, p->workspace, p->workspace_bytes, p->flags);
+                               p->max_seq_len, p->partition_size, p->workspace, p->workspace_bytes, p->flags, 0,
+                               p->shared_prefix_tokens);
   if (r != PKV_OK) return r;
   if (L.empty) return PKV_OK;
   const void* slots = nullptr;

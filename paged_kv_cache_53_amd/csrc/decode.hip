@@ -369,6 +369,107 @@ __device__ inline void vload(unsigned& d, const void* p) {
   else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const unsigned*>(p));
   else d = *static_cast<const unsigned*>(p);
 }
+// Per-tile choice of the load policy: a group of loads issued in one asm statement whose one scalar
+// branch picks the cacheable or the non-temporal form of every load (cached: wave-uniform, nonzero for
+// cacheable).  Both paths issue the same loads into the same registers, so the statement counts the
+// same on vmcnt either way, and the compiler sees a single definition of each register: two separate
+// load sequences under a branch of its own meet in a merge that it may resolve by copying the loaded
+// registers before the data arrives.  (Explicitly waited kernels only.)
+__device__ inline void vload_sel(u32x4& d0, u32x4& d1, const void* p0, const void* p1, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %4, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx4 %0, %2, off\n\t"
+      "global_load_dwordx4 %1, %3, off\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx4 %0, %2, off nt\n\t"
+      "global_load_dwordx4 %1, %3, off nt\n"
+      "2:"
+      : "+v"(d0), "+v"(d1)
+      : "v"(p0), "v"(p1), "s"(c)
+      : "scc");
+}
+__device__ inline void vload_sel(u32x4& d0, u32x4& d1, u32x4& d2, u32x4& d3, const void* p0, const void* p1, const void* p2, const void* p3, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %8, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx4 %0, %4, off\n\t"
+      "global_load_dwordx4 %1, %5, off\n\t"
+      "global_load_dwordx4 %2, %6, off\n\t"
+      "global_load_dwordx4 %3, %7, off\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx4 %0, %4, off nt\n\t"
+      "global_load_dwordx4 %1, %5, off nt\n\t"
+      "global_load_dwordx4 %2, %6, off nt\n\t"
+      "global_load_dwordx4 %3, %7, off nt\n"
+      "2:"
+      : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "s"(c)
+      : "scc");
+}
+__device__ inline void vload_sel(u32x2& d0, u32x2& d1, u32x2& d2, u32x2& d3, const void* p0, const void* p1, const void* p2, const void* p3, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %8, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx2 %0, %4, off\n\t"
+      "global_load_dwordx2 %1, %5, off\n\t"
+      "global_load_dwordx2 %2, %6, off\n\t"
+      "global_load_dwordx2 %3, %7, off\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx2 %0, %4, off nt\n\t"
+      "global_load_dwordx2 %1, %5, off nt\n\t"
+      "global_load_dwordx2 %2, %6, off nt\n\t"
+      "global_load_dwordx2 %3, %7, off nt\n"
+      "2:"
+      : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "s"(c)
+      : "scc");
+}
+__device__ inline void vload_sel(u32x2& d0, u32x2& d1, u32x2& d2, u32x2& d3, u32x2& d4, u32x2& d5, u32x2& d6, u32x2& d7, const void* p0, const void* p1, const void* p2, const void* p3, const void* p4, const void* p5, const void* p6, const void* p7, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %16, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx2 %0, %8, off\n\t"
+      "global_load_dwordx2 %1, %9, off\n\t"
+      "global_load_dwordx2 %2, %10, off\n\t"
+      "global_load_dwordx2 %3, %11, off\n\t"
+      "global_load_dwordx2 %4, %12, off\n\t"
+      "global_load_dwordx2 %5, %13, off\n\t"
+      "global_load_dwordx2 %6, %14, off\n\t"
+      "global_load_dwordx2 %7, %15, off\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx2 %0, %8, off nt\n\t"
+      "global_load_dwordx2 %1, %9, off nt\n\t"
+      "global_load_dwordx2 %2, %10, off nt\n\t"
+      "global_load_dwordx2 %3, %11, off nt\n\t"
+      "global_load_dwordx2 %4, %12, off nt\n\t"
+      "global_load_dwordx2 %5, %13, off nt\n\t"
+      "global_load_dwordx2 %6, %14, off nt\n\t"
+      "global_load_dwordx2 %7, %15, off nt\n"
+      "2:"
+      : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3), "+v"(d4), "+v"(d5), "+v"(d6), "+v"(d7)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4), "v"(p5), "v"(p6), "v"(p7), "s"(c)
+      : "scc");
+}
+template <int N> __device__ inline void vload_group(u32x4 (&d)[N], const void* const (&p)[N], unsigned c) {
+  static_assert(N == 2 || N == 4, "groups of 2 or 4 16-byte loads");
+  if constexpr (N == 2) vload_sel(d[0], d[1], p[0], p[1], c);
+  else vload_sel(d[0], d[1], d[2], d[3], p[0], p[1], p[2], p[3], c);
+}
+template <int N> __device__ inline void vload_group(u32x2 (&d)[N], const void* const (&p)[N], unsigned c) {
+  static_assert(N == 4 || N == 8, "groups of 4 or 8 8-byte loads");
+  if constexpr (N == 4) vload_sel(d[0], d[1], d[2], d[3], p[0], p[1], p[2], p[3], c);
+  else vload_sel(d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7], p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], c);
+}
+
 // waits until at most N vector-memory operations are outstanding
 // (the memory clobber keeps every memory access of the source on its side of the wait: a read of
 // LDS that a global-to-LDS load fills must not be scheduled above the wait that retires that load)
@@ -447,9 +548,9 @@ struct Tile16 {
   // Block ids are wave-uniform scalar loads (the first one was read when the unit was opened);
   // table entries past the unit's last block are never read (those tokens reuse the first id
   // and are masked in the compute).  FLAT: block i of the unit is id_first + i, no table.
-  template <int Bsz, bool E, bool NT, bool FLAT>
+  template <int Bsz, bool E, bool NT, bool FLAT, bool MIX = false>
   __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const T* kbase,
-                        const T* vbase, int t0, int64_t blk_stride) {
+                        const T* vbase, int t0, int64_t blk_stride, unsigned cached = 0) {
     constexpr int X = Kv<T>::X;
     constexpr int NB = Bsz >= 16 ? 1 : 16 / Bsz;   // blocks per tile
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
@@ -463,8 +564,15 @@ struct Tile16 {
     id1 = min(max(id1, 0), a.num_blocks - 1);
     const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
     const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
+    if constexpr (MIX) {
+      const void* ka[NK];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[ks], kb + ks * 4 * Bsz * X);
+      for (int ks = 0; ks < NK; ++ks) ka[ks] = kb + ks * 4 * Bsz * X;
+      vload_group(kf, ka, cached);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[ks], kb + ks * 4 * Bsz * X);
+    }
     const int bv = (NB == 2 && g >= 2) ? id1 : id0;
     const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
     // A block of more than 16 tokens holds each value dim's tokens in a row longer than the tile's
@@ -472,8 +580,15 @@ struct Tile16 {
     // stay cacheable (the non-temporal hint made the second half come from HBM again: 1115 us
     // instead of 840 us on the Llama-70B-class batch at B = 32).  Key lines are read whole.
     constexpr bool kNTV = NT && Bsz <= 16;
+    if constexpr (MIX) {
+      const void* va[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vload<E, kNTV>(vf[dt], vb + dt * 16 * Bsz);
+      for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
+      vload_group(vf, va, Bsz <= 16 ? cached : 1u);
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) vload<E, kNTV>(vf[dt], vb + dt * 16 * Bsz);
+    }
   }
   // orders every later use of the tile's registers after the preceding wait
   template <bool E> __device__ void tie_all() {
@@ -500,9 +615,9 @@ struct Tile32F8 {
   u32x4 kf[2][NK];
   u32x2 vf[D / 16];
 
-  template <int Bsz, bool E, bool NT, bool FLAT>
+  template <int Bsz, bool E, bool NT, bool FLAT, bool MIX = false>
   __device__ void issue(const DecodeArgs& a, const int32_t* bt, int id_first, int ntok, const E4M3* kbase,
-                        const E4M3* vbase, int t0, int64_t blk_stride) {
+                        const E4M3* vbase, int t0, int64_t blk_stride, unsigned cached = 0) {
     constexpr int NB = 32 / Bsz;                 // blocks per tile: 4, 2 or 1
     constexpr int TPB = Bsz / 8;                 // 8-token groups per block
     const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
@@ -522,6 +637,7 @@ struct Tile32F8 {
     // The previous row order (token 8(r/4) + 4b + r%4, which left the scores in the PV layout
     // directly) read every line in two 64-byte halves from two loads: 450 against 437 us on the
     // Llama-70B-class batch, where it had to keep key lines cacheable.
+    const void* ka[2 * NK];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int tt = 16 * b + r16;
@@ -531,7 +647,14 @@ struct Tile32F8 {
       for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
       const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + (tt & (Bsz - 1))) * 16;
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[b][ks], kb + ks * 4 * Bsz * 16);
+      for (int ks = 0; ks < NK; ++ks) {
+        ka[b * NK + ks] = kb + ks * 4 * Bsz * 16;
+        if constexpr (!MIX) vload<E, NT>(kf[b][ks], ka[b * NK + ks]);
+      }
+    }
+    if constexpr (MIX) {
+      u32x4(&kflat)[2 * NK] = *reinterpret_cast<u32x4(*)[2 * NK]>(&kf[0][0]);
+      vload_group(kflat, ka, cached);
     }
     // value dims: tokens 8g..8g+7 lie in block g / TPB
     const int jv = g / TPB;
@@ -539,8 +662,15 @@ struct Tile32F8 {
 #pragma unroll
     for (int j = 1; j < NB; ++j) bv = jv == j ? id[j] : bv;
     const E4M3* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((8 * g) & (Bsz - 1));
+    if constexpr (MIX) {
+      const void* va[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
+      for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
+      vload_group(vf, va, cached);
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
+    }
   }
   template <bool E> __device__ void tie_all() {
 #pragma unroll
@@ -1067,7 +1197,7 @@ __device__ inline void claim_unit(const DecodeArgs& a, int& slot) {
 // pressure of five tile buffers, which the wait check reports).
 // KV: the storage type of the pools (the tile's element); Math carries the compute type; NB: tile
 // buffers; WPE: waves per SIMD the register budget is set for.
-template <typename KV, int D, int Bsz, class Math, bool NT, bool FLAT, int NB, int WPE>
+template <typename KV, int D, int Bsz, class Math, bool NT, bool FLAT, int NB, int WPE, bool MIX>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void decode_kernel(DecodeArgs a) {
   using Tile = typename Math::Tile;
@@ -1076,6 +1206,7 @@ void decode_kernel(DecodeArgs a) {
   static_assert(NB >= 3 && NB <= 6, "tile buffers");
   // explicitly waited loads while the tile buffers fit in registers (32 per tile)
   constexpr bool E = sizeof(Tile) <= 32 * 4;
+  static_assert(!MIX || (E && !NT), "a per-tile load policy needs the explicit waits");
   constexpr int LT = Tile::kLoads;   // every step issues exactly this many tile loads
   static_assert(!E || (NB - 1) * LT < 64, "vmcnt holds 6 bits");
   // q straight into LDS needs the explicit waits: the compiler's own waits do not know of such a load
@@ -1182,10 +1313,16 @@ void decode_kernel(DecodeArgs a) {
     // may resolve by copying the loaded registers before the data arrives.
     // (unary + makes each operand a value: a select of lvalues selects their addresses, which
     // keeps the variables out of registers)
-    Y.template issue<Bsz, E, NT, FLAT>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
-                                 is_real ? +ui.ntok : +uc.ntok,
-                                 is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
-                                 is_real ? +ti : tc_now, blk_stride);
+    // MIX: tiles that start in the rows' shared prefix are read cacheable, the others streamed
+    unsigned cached = 0;
+    if constexpr (MIX) {
+      // (a filler's policy does not matter: the issue cursor's position decides it too)
+      cached = __builtin_amdgcn_readfirstlane(ui.part * a.part_tokens + ti < a.cache_tokens ? 1 : 0);
+    }
+    Y.template issue<Bsz, E, NT, FLAT, MIX>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
+                                      is_real ? +ui.ntok : +uc.ntok,
+                                      is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
+                                      is_real ? +ti : tc_now, blk_stride, cached);
     ti += is_real ? TT : 0;   // a select: a conditional update would put ti in memory
     return is_real;
   };
@@ -1317,13 +1454,13 @@ template <typename KV, class Math, bool NT> struct Pipeline {
   static constexpr int WPE = k16 ? PKV_WPE16 : k8 ? PKV_WPE8 : 2;
 };
 
-template <typename KV, int D, class Math, bool NT, bool FLAT = false>
+template <typename KV, int D, class Math, bool NT, bool FLAT = false, bool MIX = false>
 const void* kernel_ptr_b(int block_size) {
   constexpr int NB = Pipeline<KV, Math, NT>::NB, W = Pipeline<KV, Math, NT>::WPE;
   switch (block_size) {
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT, FLAT, NB, W>);
-    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT, FLAT, NB, W>);
-    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT, FLAT, NB, W>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 8, Math, NT, FLAT, NB, W, MIX>);
+    case 16: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 16, Math, NT, FLAT, NB, W, MIX>);
+    case 32: return reinterpret_cast<const void*>(&decode_kernel<KV, D, 32, Math, NT, FLAT, NB, W, MIX>);
     default: return nullptr;
   }
 }
@@ -1331,7 +1468,8 @@ const void* kernel_ptr_b(int block_size) {
 // T: the type of q and of the outputs; fp8: the pools hold E4M3 codes (MFMA path only); flat: rows
 // read consecutive blocks of their span (16-bit KV on MFMA, streamed loads only)
 template <typename T, int D>
-const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8, bool flat) {
+const void* kernel_ptr_d(int path, int group, int block_size, int pol, bool fp8, bool flat) {
+  const bool nt = pol == kLoadStreamed, mix = pol == kLoadMixed;
   if (flat) {
     if constexpr (sizeof(T) == 2)
       if (path == 1 && !fp8 && nt) return kernel_ptr_b<T, D, MfmaMath<T, D>, true, true>(block_size);
@@ -1341,13 +1479,15 @@ const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8,
     if constexpr (sizeof(T) == 2) {
       if (fp8)
         return nt ? kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, true>(block_size)
-                  : kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, false>(block_size);
+               : mix ? kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, false, false, true>(block_size)
+                     : kernel_ptr_b<E4M3, D, MfmaMath<T, D, E4M3>, false>(block_size);
       return nt ? kernel_ptr_b<T, D, MfmaMath<T, D>, true>(block_size)
-                : kernel_ptr_b<T, D, MfmaMath<T, D>, false>(block_size);
+             : mix ? kernel_ptr_b<T, D, MfmaMath<T, D>, false, false, true>(block_size)
+                   : kernel_ptr_b<T, D, MfmaMath<T, D>, false>(block_size);
     }
     return nullptr;
   }
-  if (fp8) return nullptr;
+  if (fp8 || mix) return nullptr;
   // the vector path: fp32 KV (always streamed), and 16-bit KV with G = 1 when the caller asks for it
   if constexpr (sizeof(T) == 4) {
     if (group == 1) return kernel_ptr_b<T, D, VecMath<T, D, 1>, true>(block_size);
@@ -1362,9 +1502,9 @@ const void* kernel_ptr_d(int path, int group, int block_size, bool nt, bool fp8,
 }
 
 template <typename T>
-const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, bool nt, bool fp8, bool flat) {
-  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, nt, fp8, flat)
-                         : kernel_ptr_d<T, 64>(path, group, block_size, nt, fp8, flat);
+const void* main_kernel_ptr(int head_dim, int path, int group, int block_size, int pol, bool fp8, bool flat) {
+  return head_dim == 128 ? kernel_ptr_d<T, 128>(path, group, block_size, pol, fp8, flat)
+                         : kernel_ptr_d<T, 64>(path, group, block_size, pol, fp8, flat);
 }
 
 template <typename T, int D>
@@ -1402,13 +1542,13 @@ hipError_t launch_step_prologue(const DecodeArgs& a, const ScatterArgs& sc, cons
   return hipGetLastError();
 }
 
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, bool nt,
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, int pol,
                               int32_t grid, hipStream_t st) {
   const bool flat = a.flat_bps > 0;
   const void* fn =
-      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat)
-      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat)
-                         : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, nt, kv_fp8, flat);
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, a.group, a.block_size, pol, kv_fp8, flat)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, a.group, a.block_size, pol, kv_fp8, flat)
+                         : main_kernel_ptr<__bf16>(head_dim, path, a.group, a.block_size, pol, kv_fp8, flat);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(64), args, 0, st);
@@ -1429,12 +1569,12 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hi
 }
 
 hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
-                                int block_size, bool nt, int32_t* cap) {
-  // the two cache policies have their own pipeline shapes, so their own occupancy
+                                int block_size, int pol, int32_t* cap) {
+  // the load policies have their own pipeline shapes, so their own occupancy
   const void* fn =
-      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, nt, kv_fp8, flat)
-      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, nt, kv_fp8, flat)
-                         : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, nt, kv_fp8, flat);
+      dtype == PKV_F32   ? main_kernel_ptr<float>(head_dim, path, group, block_size, pol, kv_fp8, flat)
+      : dtype == PKV_F16 ? main_kernel_ptr<_Float16>(head_dim, path, group, block_size, pol, kv_fp8, flat)
+                         : main_kernel_ptr<__bf16>(head_dim, path, group, block_size, pol, kv_fp8, flat);
   if (!fn) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

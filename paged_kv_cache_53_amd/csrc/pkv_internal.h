@@ -57,7 +57,13 @@ struct DecodeArgs {
                          // are kept in the base-2 domain
   float v_scale;         // value scale of a quantised cache (1 otherwise)
   int32_t flat_bps;      // > 0: flat spans of this many blocks, block_tables holds one span per row
+  int32_t cache_tokens;  // per-tile load policy: tiles starting before this token of their row are read
+                         // cacheable, the others streamed
 };
+
+// How the decode kernel reads the pools: every tile cacheable, every tile streamed (non-temporal), or
+// per tile (cacheable below DecodeArgs::cache_tokens).
+enum LoadPolicy { kLoadCached = 0, kLoadStreamed = 1, kLoadMixed = 2 };
 
 // The fused decode step's own arguments (beyond the scatter's and the decode's).
 struct StepArgs {
@@ -101,14 +107,13 @@ hipError_t launch_check_tables(const int32_t* tables, int32_t stride, const int3
 hipError_t launch_step_prologue(const DecodeArgs& a, const ScatterArgs& sc, const StepArgs& st, int dtype,
                                 bool kv_fp8, int head_dim, hipStream_t stream);
 // dtype: the type of q and of the results; kv_fp8: the pools hold FP8 E4M3 codes (else dtype)
-// path: 0 = vector, 1 = MFMA
-// nt: stream the key/value tiles with the non-temporal hint (otherwise ordinary cached loads)
-hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, bool nt,
+// path: 0 = vector, 1 = MFMA; pol: a LoadPolicy
+hipError_t launch_decode_main(const DecodeArgs& a, int dtype, bool kv_fp8, int head_dim, int path, int pol,
                               int32_t grid, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Persistent grid size for the main decode kernel on the current device.
 hipError_t decode_main_grid_cap(int dtype, bool kv_fp8, bool flat, int head_dim, int path, int group,
-                                int block_size, bool nt, int32_t* cap);
+                                int block_size, int pol, int32_t* cap);
 
 // Physical memory of a flat-span pool is mapped in chunks of this size unless the caller picks another.
 constexpr size_t PKV_SPAN_DEFAULT_CHUNK = size_t{2} << 20;

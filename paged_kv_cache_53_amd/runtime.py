@@ -155,10 +155,39 @@ class DecodeBatch:
         self.load_policy = "auto"   # "auto", "streamed" or "cached": how decode reads the pools
         self.vector = False         # one head per KV head on the per-token vector path (decode_only)
         self.check_tables = False   # debug mode: check the device tables before each decode (synchronises)
+        self.shared_prefix = self._find_shared_prefix()
         self._check_result = torch.empty(2, dtype=torch.int32, device=dev)
 
     STAGES = 8
     STAGE_EVENT_EVERY = 4
+
+    def _find_shared_prefix(self) -> int:
+        """Tokens at the start of the batch's rows that lie in blocks other rows also read: for each row,
+        its leading blocks whose reference count exceeds one (a prompt the rows were forked from), the
+        largest such prefix over the rows.  Appends can only shorten it (a row writes into private blocks
+        only, copying a partly filled shared block first), so the value taken when the batch is set up or
+        refreshed bounds it: tokens it covers that became private are merely read cacheable."""
+        c = self.cache
+        tables, lens = c.allocator.fill_block_tables(self.seq_ids, self.stride, pad=0)
+        best = 0
+        for r in range(self.S):
+            n = 0
+            nb = -(-int(lens[r]) // c.block_size)
+            while n < nb and c.allocator.ref_count(int(tables[r, n])) > 1:
+                n += 1
+            best = max(best, min(int(lens[r]), n * c.block_size))
+        return best
+
+    def _load_args(self) -> dict:
+        """How decode reads the pools: the shared prefix cacheable and the rest streamed when the rows
+        share a prompt, else every tile cacheable when they share other blocks, else streamed."""
+        if self.load_policy == "cached":
+            return {"shared_kv": True}
+        if self.load_policy == "streamed":
+            return {}
+        if self.load_policy == "prefix" or (self.load_policy == "auto" and self.shared_prefix > 0):
+            return {"shared_prefix_tokens": max(1, self.shared_prefix)} if self.shared_prefix else {"shared_kv": True}
+        return {"shared_kv": self.cache.has_shared_blocks()}
 
     def _keep_cached(self) -> bool:
         """Decode with cacheable loads when blocks are shared between rows (their re-reads then hit
@@ -214,14 +243,14 @@ class DecodeBatch:
         if fused:
             decode_step(out, q, k_new, v_new, self.slot_stage[i], c.k_pool, c.v_pool, self.tables, self.seq_lens,
                         self.scale, self.max_seq_len, self.partition_size, workspace=self.workspace,
-                        shared_kv=self._keep_cached(), **c.scales)
+                        **self._load_args(), **c.scales)
         else:
             self.slot_dev.copy_(self.slot_stage[i], non_blocking=True)
             append_slots(self.slot_dev, self.tables, self.seq_lens, c.block_size)
             reshape_and_cache(k_new, v_new, self.slot_dev, c.k_pool, c.v_pool, **c.scales)
             paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                    self.max_seq_len, self.partition_size, workspace=self.workspace,
-                                   shared_kv=self._keep_cached(), **c.scales)
+                                   **self._load_args(), **c.scales)
         if (self.steps + 1) % self.STAGE_EVENT_EVERY == 0:
             ev = torch.cuda.Event()
             ev.record()
@@ -235,6 +264,7 @@ class DecodeBatch:
         self.tables.copy_(torch.from_numpy(tables))
         self.seq_lens.copy_(torch.from_numpy(lens.copy()))
         self.host_lens = lens.astype(np.int64)
+        self.shared_prefix = self._find_shared_prefix()
 
     def decode_only(self, q: torch.Tensor, out: torch.Tensor) -> None:
         """Attention over the current tokens without appending (no host work, no scatter)."""
@@ -243,7 +273,7 @@ class DecodeBatch:
         c = self.cache
         paged_attention_decode(out, q, c.k_pool, c.v_pool, self.tables, self.seq_lens, self.scale,
                                self.max_seq_len, self.partition_size, workspace=self.workspace,
-                               shared_kv=self._keep_cached(), vector=self.vector, **c.scales)
+                               vector=self.vector, **self._load_args(), **c.scales)
 
 
 class FlatKVCache:

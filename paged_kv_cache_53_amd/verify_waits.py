@@ -72,10 +72,36 @@ class _Insn:
         self.asm_dst = self.writes if (asm and self.vmem and self.writes) else set()
 
 
+def _asm_local_labels(body: List[str]):
+    """Numeric local labels ("1:") inside inline-assembly regions, and the resolution of each branch to
+    one ("1f": the next such label, "1b": the previous one), as unique block names "asm<line>"."""
+    in_asm, defs = False, []
+    for i, raw in enumerate(body):
+        t = raw.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif in_asm and re.match(r"^\d+:$", t.split(";")[0].strip()):
+            defs.append((i, t.split(";")[0].strip()[:-1]))
+
+    def resolve(i: int, ref: str) -> Optional[str]:
+        m = re.match(r"^(\d+)([fb])$", ref)
+        if not m:
+            return None
+        num, d = m.group(1), m.group(2)
+        cands = [j for j, n in defs if n == num and (j > i if d == "f" else j < i)]
+        if not cands:
+            return None
+        return f"asm{min(cands) if d == 'f' else max(cands)}"
+    return {i for i, _ in defs}, resolve
+
+
 def _kernel_blocks(body: List[str]):
     """Basic blocks: (label, [insn], successors by label, falls_through)."""
     blocks: List[Tuple[str, List[_Insn], List[str], bool]] = []
     label, insns, in_asm, n = "entry", [], False, 0
+    asm_labels, resolve = _asm_local_labels(body)
 
     def close(next_label: Optional[str]):
         nonlocal label, insns, n
@@ -84,8 +110,11 @@ def _kernel_blocks(body: List[str]):
         n += 1
         insns = []
 
-    for raw in body:
+    for li, raw in enumerate(body):
         t = raw.split(";")[0].strip() if not raw.strip().startswith(";;#ASM") else raw.strip()
+        if li in asm_labels:
+            close(f"asm{li}")
+            continue
         if raw.strip().startswith(";;#ASMSTART"):
             in_asm = True
             continue
@@ -103,6 +132,11 @@ def _kernel_blocks(body: List[str]):
         if not t or t.startswith("."):
             continue
         ins = _Insn(t, in_asm)
+        if in_asm and (ins.op == "s_branch" or ins.op.startswith("s_cbranch")):
+            target = resolve(li, ins.text.split()[1])
+            if target is None:
+                raise RuntimeError(f"inline-assembly branch with no local label: {ins.text}")
+            ins.text = f"{ins.op} {target}"
         insns.append(ins)
         if ins.op in ("s_branch", "s_endpgm", "s_setpc_b64") or ins.op.startswith("s_cbranch"):
             close(None)

@@ -100,7 +100,7 @@ class GpuState:
         torch.cuda.synchronize()
 
     def decode(self, out_dtype=None, partition_size=None, max_seq_len=None, q=None, workspace=None,
-               shared_kv=False, scales=None, vector=False):
+               shared_kv=False, scales=None, vector=False, shared_prefix_tokens=0):
         w = self.w
         odt = TORCH_DTYPE[w.dtype] if out_dtype is None else out_dtype
         q = self.q if q is None else q
@@ -109,6 +109,7 @@ class GpuState:
                                         w.scale, w.max_seq_len if max_seq_len is None else max_seq_len,
                                         w.partition_size if partition_size is None else partition_size,
                                         workspace=workspace, shared_kv=shared_kv, vector=vector,
+                                        shared_prefix_tokens=shared_prefix_tokens,
                                         **(self.scales if scales is None else scales))
         torch.cuda.synchronize()
         return out

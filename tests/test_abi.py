@@ -34,7 +34,7 @@ def test_status_strings_and_version():
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(-2).decode() == "out of KV-cache blocks"
-    assert lib.pkv_version() == 1
+    assert lib.pkv_version() == 2
 
 
 def test_pool_bytes():

@@ -65,8 +65,11 @@ def test_shared_prefix_equals_copied_prefix_bitwise():
     assert a.alloc.stats()["shared_blocks"] == 400 // 16
     oa, ob = a.decode(), b.decode()
     assert torch.equal(_bits(oa), _bits(ob))
-    # the cache-policy flag (kept-cacheable loads for shared blocks) changes no bit of the result
+    # the load policy (every tile cacheable, or only the shared prompt's, at various prefix lengths)
+    # changes no bit of the result
     assert torch.equal(_bits(a.decode(shared_kv=True)), _bits(oa))
+    for n in (400, 16, 417, 100000):
+        assert torch.equal(_bits(a.decode(shared_prefix_tokens=n)), _bits(oa)), n
     ref = oracle_rows(copied, range(copied.num_seqs))
     assert max_abs_err(oa, ref, rows=range(copied.num_seqs)) <= TOL["f16"]
 
@@ -271,11 +274,13 @@ def test_full_size_shared_prefix_equals_copied_prefix_bitwise():
     a = GpuState(shared, poison=True)
     assert a.alloc.stats()["shared_blocks"] == 250
     oa, oa_cached = a.decode(), a.decode(shared_kv=True)
+    oa_prefix = a.decode(shared_prefix_tokens=4000)
     del a
     torch.cuda.empty_cache()
     b = GpuState(copied, poison=True)
     assert b.alloc.stats()["shared_blocks"] == 0
     ob = b.decode()
+    assert torch.equal(_bits(oa_prefix), _bits(oa))
     del b
     torch.cuda.empty_cache()
     assert torch.equal(_bits(oa), _bits(ob))

@@ -164,6 +164,9 @@ def test_fp8_shared_prefix_cache_policy_changes_no_bit():
     a = st.decode()
     b = st.decode(shared_kv=True)
     assert torch.equal(a.view(torch.int16).cpu(), b.view(torch.int16).cpu())
+    for n in (400, 32, 100000):
+        c = st.decode(shared_prefix_tokens=n)
+        assert torch.equal(a.view(torch.int16).cpu(), c.view(torch.int16).cpu()), n
     ref = oracle_rows(w, range(w.num_seqs))
     assert max_abs_err(a, ref, rows=range(w.num_seqs)) <= TOL[w.dtype]
 
@@ -230,6 +233,7 @@ def test_fp8_full_size_shared_prefix_equals_copied_prefix_bitwise():
     a = GpuState(shared, poison=True)
     assert a.alloc.stats()["shared_blocks"] == 250
     oa, oa_cached = a.decode(), a.decode(shared_kv=True)
+    assert torch.equal(a.decode(shared_prefix_tokens=4000).view(torch.int16).cpu(), oa.view(torch.int16).cpu())
     del a
     torch.cuda.empty_cache()
     b = GpuState(copied, poison=True)

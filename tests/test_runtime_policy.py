@@ -1,8 +1,9 @@
 """The decode batch's load policy, on the CPU with a stand-in cache.
 
 Decode reads the pools with cacheable loads only when some block is shared between rows (forks, a
-shared prompt), whose re-reads then hit in L2 and the Infinity Cache; every other batch, FP8 or
-16-bit, small or large, is streamed with the non-temporal hint.  `load_policy` overrides the rule.
+shared prompt), whose re-reads then hit in L2 and the Infinity Cache; when the sharing is a prefix of
+the rows, only the tiles of that prefix are read cacheable and the rest streamed.  Every other batch,
+FP8 or 16-bit, small or large, is streamed with the non-temporal hint.  `load_policy` overrides the rule.
 """
 import types
 
@@ -11,10 +12,10 @@ import pytest
 from paged_kv_cache_53_amd.runtime import DecodeBatch
 
 
-def _batch(shared, quantised, tokens, policy="auto"):
+def _batch(shared, quantised, tokens, policy="auto", prefix=0):
     cache = types.SimpleNamespace(has_shared_blocks=lambda: shared, quantised=quantised, n_kv_heads=8,
                                   head_dim=128)
-    return types.SimpleNamespace(cache=cache, load_policy=policy, host_lens=[tokens])
+    return types.SimpleNamespace(cache=cache, load_policy=policy, host_lens=[tokens], shared_prefix=prefix)
 
 
 @pytest.mark.parametrize("quantised", [False, True])
@@ -30,3 +31,32 @@ def test_shared_blocks_alone_select_cacheable_loads(quantised, tokens):
 def test_policy_override(shared):
     assert DecodeBatch._keep_cached(_batch(shared, False, 100, "cached")) is True
     assert DecodeBatch._keep_cached(_batch(shared, True, 100, "streamed")) is False
+
+
+def test_shared_prefix_is_read_cacheable_and_the_rest_streamed():
+    b = _batch(True, False, 16000, prefix=4000)
+    assert DecodeBatch._load_args(b) == {"shared_prefix_tokens": 4000}
+    # shared blocks that are no prefix of the rows: every tile cacheable
+    assert DecodeBatch._load_args(_batch(True, False, 100)) == {"shared_kv": True}
+    assert DecodeBatch._load_args(_batch(False, False, 100)) == {"shared_kv": False}
+    assert DecodeBatch._load_args(_batch(True, False, 100, "cached", prefix=64)) == {"shared_kv": True}
+    assert DecodeBatch._load_args(_batch(True, False, 100, "streamed", prefix=64)) == {}
+
+
+def test_shared_prefix_from_reference_counts():
+    """The prefix is taken from the allocator: leading blocks of a row with more than one reference."""
+    import numpy as np
+    from paged_kv_cache_53_amd import Allocator
+    a = Allocator(64, 16)
+    a.alloc(9, 40)                       # a 40-token prompt: blocks 0, 1 full, block 2 with 8 tokens
+    for c in (0, 1):
+        a.fork(9, c, 32)                 # the children share its two full blocks
+        a.alloc(c, 5)
+    a.free(9)
+    b = types.SimpleNamespace(cache=types.SimpleNamespace(allocator=a, block_size=16), S=2,
+                              seq_ids=np.array([0, 1], dtype=np.int64), stride=4)
+    assert DecodeBatch._find_shared_prefix(b) == 32
+    a.alloc(2, 50)                       # a row of its own: no shared prefix
+    b2 = types.SimpleNamespace(cache=types.SimpleNamespace(allocator=a, block_size=16), S=1,
+                               seq_ids=np.array([2], dtype=np.int64), stride=4)
+    assert DecodeBatch._find_shared_prefix(b2) == 0

@@ -181,6 +181,40 @@ def test_accumulation_registers_are_tracked():
     assert _check(body.replace("v_accvgpr_read_b32 v8, a4", "v_mov_b32_e32 v8, v4")) == []
 
 
+def test_branches_inside_inline_assembly_are_followed():
+    # one asm statement choosing between two load forms: both paths load v[4:7], one instruction each
+    two_paths = """
+;;#ASMSTART
+\ts_cmp_eq_u32 s6, 0
+\ts_cbranch_scc1 1f
+\tglobal_load_dwordx4 v[4:7], v[0:1], off
+\ts_branch 2f
+1:
+\tglobal_load_dwordx4 v[4:7], v[0:1], off nt
+2:
+;;#ASMEND
+{wait}
+\tv_mov_b32_e32 v20, v4
+\ts_endpgm
+"""
+    assert _check(two_paths.format(wait=_asm("s_waitcnt vmcnt(0)"))) == []
+    assert len(_check(two_paths.format(wait=""))) == 1
+    # a path that loads nothing more: the wait count that suffices on the other path is then too loose
+    uneven = """
+{load}
+;;#ASMSTART
+\ts_cmp_eq_u32 s6, 0
+\ts_cbranch_scc1 1f
+\tglobal_load_dwordx4 v[8:11], v[0:1], off
+1:
+;;#ASMEND
+{wait}
+\tv_mov_b32_e32 v20, v4
+\ts_endpgm
+""".format(load=_asm("global_load_dwordx4 v[4:7], v[0:1], off"), wait=_asm("s_waitcnt vmcnt(1)"))
+    assert len(_check(uneven)) == 1
+
+
 def test_built_decode_kernels_pass():
     path = os.path.join(ROOT, "paged_kv_cache_53_amd", "_build", "decode.s")
     if not os.path.exists(path):
