@@ -151,6 +151,23 @@ def build_batch(w, fill="randn", extra_tokens=0, layout="paged", chunk_bytes=0):
     return cache, batch
 
 
+def host_duplicate_tokens(w):
+    """duplicate_tokens of the workload's prompt batch, from its allocator operations replayed on a host
+    allocator alone (no device memory: the counter summaries are made on the CPU)."""
+    from paged_kv_cache_53_amd import Allocator
+    alloc = Allocator(w.num_blocks, w.block_size, w.free_order.tolist())
+    for op in w.prompt_ops:
+        if op["op"] == "alloc":
+            alloc.alloc(op["seq"], op["n"])
+        elif op["op"] == "fork":
+            alloc.fork(op["parent"], op["child"], op["n"])
+        else:
+            alloc.free(op["seq"])
+    stride = -(-(int(w.seq_lens.max()) + 64) // w.block_size)
+    tables, _ = alloc.fill_block_tables(w.batch.tolist(), stride, pad=0)
+    return duplicate_tokens(tables, w.seq_lens - 1, w.block_size)
+
+
 def kv_bytes(w, lens, table=True):
     """Algorithmic bytes one decode reads: K+V of every valid token, plus the block-table entries
     (none for flat spans)."""
@@ -497,10 +514,13 @@ def pmc_summary(args):
     # decode dispatch j of the profiled bench run attends over the prompt (L - 1 tokens) plus the
     # j + 1 tokens appended so far; a --decode-only run appends nothing
     prompt = w.seq_lens.astype(np.int64) - 1
+    # unique bytes, as the bench line's roofline counts them: a block several rows read counts once
+    # (appended tokens go to private blocks, so the duplicates stay those of the prompt)
+    dup_bytes = host_duplicate_tokens(w) * 2 * w.n_kv_heads * w.head_dim * w.kv_esize
 
     def algo(j):
         kvb, tb = kv_bytes(w, prompt if args.decode_only else prompt + j + 1)
-        return kvb + tb
+        return kvb - dup_bytes + tb
 
     f_ratio = statistics.median(v * f_scale * 1024 / algo(j) for j, v in enumerate(f_vals))
     w_ratio = statistics.median(v * w_scale * 1024 / algo(j) for j, v in enumerate(w_vals))
@@ -514,6 +534,7 @@ def pmc_summary(args):
         "calibration": {"copy_bytes": 1 << 30, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
         "fetch_over_algorithmic": round(f_ratio, 5), "write_over_algorithmic": round(w_ratio, 5),
         "traffic_over_algorithmic": round(f_ratio + w_ratio, 5),
+        "duplicate_bytes_per_launch": int(dup_bytes),
         "last_launch": {"algorithmic_bytes": int(a_last), "fetch_bytes": int(f_vals[-1] * f_scale * 1024),
                         "write_bytes": int(w_vals[-1] * w_scale * 1024)},
         "command": args.pmc_command,

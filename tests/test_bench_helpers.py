@@ -65,3 +65,14 @@ def test_duplicate_tokens_counts_shared_blocks_once():
     assert bench.duplicate_tokens([[0, 1], [2]], [20, 9], B) == 0
     # a shared partial block counts its longest reader's valid tokens once
     assert bench.duplicate_tokens([[0, 1], [0, 1]], [24, 20], B) == 16 + 4
+
+
+def test_host_replay_counts_the_swarm_prompt_once_per_extra_row():
+    """The counter summaries price traffic against unique bytes: replaying the swarm's allocator
+    operations on the host finds 19 extra readings of the 4000-token prompt (250 whole blocks) and
+    none when every row holds its own copy."""
+    import workloads as wl
+    assert bench.host_duplicate_tokens(wl.build(4)) == 19 * 4000
+    assert bench.host_duplicate_tokens(wl.build(4, copied_prefix=True)) == 0
+    assert bench.host_duplicate_tokens(wl.build(4, block_size=32)) == 19 * 4000
+    assert bench.host_duplicate_tokens(wl.build(3)) == 0
