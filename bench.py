@@ -831,18 +831,24 @@ def bench_swap(args):
 
 def sweep(args):
     """long_context decode over block sizes: paged with random and identity placement, and flat spans
-    (no block table) with 2 MiB and 64 KiB chunks.  The paged-over-flat ratio is the cost of reading
-    through a block table."""
+    (no block table) with 2 MiB and 256 KiB chunks, at the launch's partition size; and paged with random
+    placement in 512-token partitions (128 per row, the split the workload states).  The paged-over-flat
+    ratio is the cost of reading through a block table."""
     import torch
 
     import workloads as wl
     rows = []
     for B in (8, 16, 32):
         per = {}
-        for layout, placement, chunk in (("paged", "random", 0), ("paged", "identity", 0), ("flat", "random", 0),
-                                         ("flat", "random", 256 << 10)):
-            w = wl.build(5, block_size=B, placement=placement, partition_size=args.partition_size)
+        for layout, placement, chunk, part in (("paged", "random", 0, args.partition_size),
+                                               ("paged", "identity", 0, args.partition_size),
+                                               ("flat", "random", 0, args.partition_size),
+                                               ("flat", "random", 256 << 10, args.partition_size),
+                                               ("paged", "random", 0, 512)):
+            w = wl.build(5, block_size=B, placement=placement, partition_size=part)
             key = placement if layout == "paged" else f"flat_{(chunk or 2 << 20) >> 10}KiB"
+            if part == 512 and args.partition_size != 512:
+                key = "random_P512"
             try:
                 res = time_steps(w, args.steps, args.warmup, decode_only=True, layout=layout, chunk_bytes=chunk,
                                  reps=0)
@@ -863,10 +869,12 @@ def sweep(args):
                 return round(per[a]["decode_us"] / per[b]["decode_us"], 4)
             return None
         rows.append({"block_size": B, **per, "random_over_identity": ratio("random", "identity"),
-                     "random_over_flat": ratio("random", "flat_2048KiB")})
-    print(json.dumps({"sweep": f"long_context 8 x 65536, bf16, 64q/8kv heads, P={w.partition_size}; decode us "
-                               "(lower is better); GB/s count K+V plus table bytes (none for flat)", "rows": rows}),
-          flush=True)
+                     "random_over_flat": ratio("random", "flat_2048KiB"),
+                     "P512_over_P": ratio("random_P512", "random")})
+    P = args.partition_size or wl.build(5, small=True).partition_size
+    print(json.dumps({"sweep": f"long_context 8 x 65536, bf16, 64q/8kv heads, P={P} (random_P512: P=512); "
+                               "decode us (lower is better); GB/s count K+V plus table bytes (none for flat)",
+                      "rows": rows}), flush=True)
 
 
 if __name__ == "__main__":
