@@ -180,7 +180,11 @@ class DecodeBatch:
 
     def _load_args(self) -> dict:
         """How decode reads the pools: the shared prefix cacheable and the rest streamed when the rows
-        share a prompt, else every tile cacheable when they share other blocks, else streamed."""
+        share a prompt, else every tile cacheable when they share other blocks, else streamed.  Measured
+        on MI355X, decode us warm / after a 1 GiB write: the shared-prompt swarm 83 / 105 with the prefix
+        policy, 88 / 143 every tile cacheable, 116 / 119 streamed; without sharing, streamed loads were as
+        fast or faster (bf16 Llama-70B-class 753 / 769 against 845 / 910 cacheable): cacheable loads
+        evict dirty lines and pay their write-back."""
         if self.load_policy == "cached":
             return {"shared_kv": True}
         if self.load_policy == "streamed":
@@ -188,17 +192,6 @@ class DecodeBatch:
         if self.load_policy == "prefix" or (self.load_policy == "auto" and self.shared_prefix > 0):
             return {"shared_prefix_tokens": max(1, self.shared_prefix)} if self.shared_prefix else {"shared_kv": True}
         return {"shared_kv": self.cache.has_shared_blocks()}
-
-    def _keep_cached(self) -> bool:
-        """Decode with cacheable loads when blocks are shared between rows (their re-reads then hit
-        L2 and the Infinity Cache), else stream with the non-temporal hint.  Measured on MI355X,
-        decode us with each launch after a 1 GiB read / after a 1 GiB write: the shared-prefix swarm
-        88 / 143 cacheable against 120 / 120 streamed; without sharing, streamed loads were as fast
-        or faster (FP8 opt13b-class batch 86 / 87 against 86 / 128 cacheable, bf16 Llama-70B-class
-        764 / 772 against 840 / 904): cacheable loads evict dirty lines and pay their write-back."""
-        if self.load_policy != "auto":
-            return self.load_policy == "cached"
-        return self.cache.has_shared_blocks()
 
     def _stage_for(self, n: int) -> int:
         """The stage of step n, once the step that last read it (n - STAGES) has finished."""

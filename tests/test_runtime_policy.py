@@ -21,16 +21,16 @@ def _batch(shared, quantised, tokens, policy="auto", prefix=0):
 @pytest.mark.parametrize("quantised", [False, True])
 @pytest.mark.parametrize("tokens", [16, 35_000, 1_200_000])
 def test_shared_blocks_alone_select_cacheable_loads(quantised, tokens):
-    assert DecodeBatch._keep_cached(_batch(True, quantised, tokens)) is True
-    # a small FP8 batch no longer stays cacheable: streamed loads lost nothing after a read and
+    assert DecodeBatch._load_args(_batch(True, quantised, tokens)) == {"shared_kv": True}
+    # a small FP8 batch does not stay cacheable: streamed loads lost nothing after a read and
     # cacheable ones lost 48 % after a write
-    assert DecodeBatch._keep_cached(_batch(False, quantised, tokens)) is False
+    assert DecodeBatch._load_args(_batch(False, quantised, tokens)) == {"shared_kv": False}
 
 
 @pytest.mark.parametrize("shared", [False, True])
 def test_policy_override(shared):
-    assert DecodeBatch._keep_cached(_batch(shared, False, 100, "cached")) is True
-    assert DecodeBatch._keep_cached(_batch(shared, True, 100, "streamed")) is False
+    assert DecodeBatch._load_args(_batch(shared, False, 100, "cached")) == {"shared_kv": True}
+    assert DecodeBatch._load_args(_batch(shared, True, 100, "streamed")) == {}
 
 
 def test_shared_prefix_is_read_cacheable_and_the_rest_streamed():
