@@ -13,7 +13,9 @@ The default workload is the Llama-3-70B-class layer: 256 sequences,
 log-normal lengths (median 3000, clipped to [16, 32768]), 64 q / 8 KV heads,
 head_dim 128, bf16 KV, 16-token blocks scattered through the pool, 3072-token
 partitions.  All inputs are the seeded synthetic workload, resident in HBM
-before the timed region.
+before the timed region.  Order of work: the batch is built, the streaming-read
+probe runs (unless --no-read-ceiling), then the W warm-up steps and, with no
+host work in between, the K timed steps.
 
 Prints one JSON line: value = algorithmic KV-read GB/s over whole steps
 (K + V bytes of every valid token plus block-table bytes), with seqs/s, the
@@ -214,7 +216,13 @@ def percentiles_us(ms_values):
 
 
 def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=0, fused=True, reps=20,
-               flush=False, load_policy="auto", math="mfma", shared_prefix_tokens=None):
+               flush=False, load_policy="auto", math="mfma", shared_prefix_tokens=None, before_warmup=None):
+    """Times `steps` decode steps of workload w after `warmup` untimed ones.  before_warmup: GPU work run
+    once the batch is resident, right before the warm-up steps (the bench line's streaming-read probe).
+    Nothing the host computes runs between the warm-up and the timed steps: an idle GPU that resumes
+    work shows a clock transient for several milliseconds (decode launches 3 to 11 after resuming took
+    800-870 us instead of about 750 on the Llama-70B-class batch), which a gap there would put into the
+    timed region."""
     import numpy as np
     import torch
 
@@ -245,18 +253,18 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
         else:
             batch.step(q, kn, vn, out)
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    lens0 = batch.host_lens.copy()
     dup = 0
     if layout == "paged":
-        tables0, _ = cache.allocator.fill_block_tables(batch.seq_ids, batch.stride, pad=0)
-        dup = duplicate_tokens(tables0, lens0, w.block_size)   # appends go to private blocks: constant
+        tables0, lens_now = cache.allocator.fill_block_tables(batch.seq_ids, batch.stride, pad=0)
+        dup = duplicate_tokens(tables0, lens_now, w.block_size)   # appends go to private blocks: constant
+    extra_gpu = before_warmup() if before_warmup is not None else None
+    for _ in range(warmup):
+        one()
     # timed region: only the decode kernel carries an event pair (each pair costs the stream a few us)
     pkv.timing_select(["decode"])
     pkv.timing_enable(True)
     torch.cuda.synchronize()
+    lens0 = batch.host_lens.copy()
     t0 = time.perf_counter()
     for _ in range(steps):
         one()
@@ -321,7 +329,7 @@ def time_steps(w, steps, warmup, decode_only=False, layout="paged", chunk_bytes=
             "lens0": lens0, "decode_timed": decode_timed, "diag_steps": diag,
             "decode_loads": load_description(batch) if layout == "paged" else "streamed",
             "decode_launch_us": percentiles_us(warm) if warm else None,
-            "decode_launch_us_cold": cold or None}
+            "decode_launch_us_cold": cold or None, "before_warmup": extra_gpu}
 
 
 def _read_text(path):
@@ -670,9 +678,17 @@ def main():
         return bench_swap(args)
 
     w = make_workload(args)
+
+    def probe():
+        # the streaming-read probe runs right before the warm-up steps: about 30 ms of full-bandwidth
+        # reads, after which the engine clock has settled under load
+        log("streaming-read probe ...")
+        return read_ceiling(full=False)
+
     res = time_steps(w, args.steps, args.warmup, decode_only=args.decode_only, layout=args.layout,
                      chunk_bytes=args.chunk_bytes, fused=not args.unfused, reps=args.reps, flush=args.flush,
-                     load_policy=args.load_policy, math=args.math, shared_prefix_tokens=args.shared_prefix_tokens)
+                     load_policy=args.load_policy, math=args.math, shared_prefix_tokens=args.shared_prefix_tokens,
+                     before_warmup=None if args.no_read_ceiling else probe)
     total_s = res["total_s"]
     gbps = (res["kv_bytes_unique"] + res["table_bytes"]) / total_s / 1e9
     gbps_logical = (res["kv_bytes"] + res["table_bytes"]) / total_s / 1e9
@@ -710,8 +726,7 @@ def main():
         line["bytes_note"] = (f"{res['duplicate_tokens']} tokens per step are read by more than one row; value, "
                               "pct_hbm_peak and roofline count each physical block once (unique bytes)")
     if not args.no_read_ceiling:
-        log("streaming-read probe ...")
-        rc = read_ceiling(full=False)
+        rc = res["before_warmup"]
         line["measured_read_gbps"] = rc["best_gbps"]
         line["read_ceiling"] = {k: rc[k] for k in ("best", "note")}
     if not args.no_cpu_baseline:
