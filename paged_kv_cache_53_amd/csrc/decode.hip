@@ -837,6 +837,15 @@ struct MfmaMath {
     const int r16 = threadIdx.x & 15;
     load_q_head_lds<T, KV, D>(a, u.s, u.kvh * a.group + (r16 < a.group ? r16 : 0), slot[0]);
   }
+  // Rescales the accumulators by alpha = 2^(old max - new max) when some lane's running max rose.
+  // Otherwise every lane's alpha is exactly 1 (v_exp_f32 of 0), so skipping the multiply changes no
+  // bit; once a row's leading tiles have passed the max rarely rises, and the skip saves reading each
+  // accumulator out of its matrix-core registers, multiplying and writing it back on most tiles.
+  __device__ void rescale(float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) == 0) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = acc[dt] * alpha;
+  }
   __device__ void compute(const Tile& R, const u32x4 (*q_lds)[NQ][64], int t0, int ntok, float scale_log2) {
     if constexpr (kQuant) compute32(R, q_lds, t0, ntok, scale_log2);
     else compute16(R, q_lds, t0, ntok, scale_log2);
@@ -876,6 +885,7 @@ struct MfmaMath {
       psum += to_f32(pt[i]);
     }
     l_run = l_run * alpha + psum;
+    rescale(alpha);
     u32x2 pb;
     __builtin_memcpy(&pb, pt, 8);
 #pragma unroll
@@ -889,7 +899,7 @@ struct MfmaMath {
           if (t0 + 4 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
         __builtin_memcpy(&va, vt, 8);
       }
-      acc[dt] = mfma_16x16x16(va, pb, acc[dt] * alpha, T{});
+      acc[dt] = mfma_16x16x16(va, pb, acc[dt], T{});
     }
   }
   // 32 tokens of FP8 codes widened to T: two 16-row QK blocks per 32 dims, then one 32-deep
@@ -937,6 +947,7 @@ struct MfmaMath {
       psum += to_f32(pt[i]);
     }
     l_run = l_run * alpha + psum;
+    rescale(alpha);
     // From the QK layout (pw[0..1]: tokens 4g..4g+3, pw[2..3]: tokens 16+4g..16+4g+3) to the PV
     // layout (tokens 8g..8g+7): the half swap gives rows g < 2 the first words of row g+2 as their
     // second words and rows g >= 2 the second words of row g-2 as their first; the row swap then
@@ -968,7 +979,7 @@ struct MfmaMath {
           if (t0 + 8 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
         __builtin_memcpy(&va, vt, 16);
       }
-      acc[dt] = mfma_16x16x32(va, pb, acc[dt] * alpha);
+      acc[dt] = mfma_16x16x32(va, pb, acc[dt]);
     }
   }
   // the normalised output when the row has one partition, else (max, sum, accumulator); with
