@@ -888,18 +888,23 @@ struct MfmaMath {
     rescale(alpha);
     u32x2 pb;
     __builtin_memcpy(&pb, pt, 8);
+    // (the partial-tile test is taken once per tile, outside the value loop, so a full tile's value
+    // products issue back to back)
+    if (partial) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 va = R.vf[dt];
-      if (partial) {
+      for (int dt = 0; dt < D / 16; ++dt) {
+        u32x2 va = R.vf[dt];
         T vt[4];
         __builtin_memcpy(vt, &va, 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (t0 + 4 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
         __builtin_memcpy(&va, vt, 8);
+        acc[dt] = mfma_16x16x16(va, pb, acc[dt], T{});
       }
-      acc[dt] = mfma_16x16x16(va, pb, acc[dt], T{});
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x16(R.vf[dt], pb, acc[dt], T{});
     }
   }
   // 32 tokens of FP8 codes widened to T: two 16-row QK blocks per 32 dims, then one 32-deep
@@ -968,18 +973,21 @@ struct MfmaMath {
     }
     V8 pb;
     __builtin_memcpy(&pb, pw, 16);
+    if (partial) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      V8 va = widen8<T>(R.vf[dt][0], R.vf[dt][1]);
-      if (partial) {
+      for (int dt = 0; dt < D / 16; ++dt) {
+        V8 va = widen8<T>(R.vf[dt][0], R.vf[dt][1]);
         T vt[8];
         __builtin_memcpy(vt, &va, 16);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (t0 + 8 * g + i >= ntok) vt[i] = static_cast<T>(0.f);
         __builtin_memcpy(&va, vt, 16);
+        acc[dt] = mfma_16x16x32(va, pb, acc[dt]);
       }
-      acc[dt] = mfma_16x16x32(va, pb, acc[dt]);
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x32(widen8<T>(R.vf[dt][0], R.vf[dt][1]), pb, acc[dt]);
     }
   }
   // the normalised output when the row has one partition, else (max, sum, accumulator); with
