@@ -21,9 +21,9 @@ Prints one JSON line: value = algorithmic KV-read GB/s over whole steps
 (K + V bytes of every valid token plus block-table bytes), with seqs/s, the
 decode kernel's roofline (HIP events on the kernel's stream), the decode
 kernel's per-launch median / p10 / p90 over separately collected launches
-after the timed region (--flush adds the same over launches that each follow
-a 1 GiB write, and over launches that each follow a 1 GiB read: either evicts
-L2 and the 256 MB Infinity Cache), the device,
+after the timed region and the same over launches that each follow a 1 GiB
+write and over launches that each follow a 1 GiB read (either evicts L2 and
+the 256 MB Infinity Cache; --no-flush leaves these out), the device,
 engine clock and ROCm version, and the fp64 CPU oracle timed on a bounded
 sample of the same workload.
 
@@ -81,9 +81,11 @@ def parse():
                    help="separately collected launches for the decode kernel's median / p10 / p90")
     p.add_argument("--load-policy", default="auto", choices=["auto", "streamed", "cached", "prefix"],
                    help="how decode reads the pools (auto: the runtime's rule)")
-    p.add_argument("--flush", action="store_true",
+    p.add_argument("--flush", dest="flush", action="store_true", default=True,
                    help="also time --reps launches after a 1 GiB write and --reps after a 1 GiB read "
-                        "(each evicts L2 and MALL)")
+                        "(each evicts L2 and MALL; the default)")
+    p.add_argument("--no-flush", dest="flush", action="store_false",
+                   help="leave out the cache-evicted launches")
     p.add_argument("--unfused", action="store_true",
                    help="paged steps as separate calls (slot copy, append_slots, scatter, decode) instead of "
                         "one decode_step")
