@@ -646,7 +646,7 @@ def main():
         return pmc_summary(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by sequence "
-              "or KV head with no exchange, but this build measures the one-GPU share", file=sys.stderr)
+              "or KV head with no exchange, and this benchmark measures one GPU's share", file=sys.stderr)
         sys.exit(2)
     import torch
 

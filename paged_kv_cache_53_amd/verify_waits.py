@@ -1,4 +1,4 @@
-"""Static check of the decode kernel's explicitly waited loads, run on the assembly of this build.
+"""Static check of the decode kernel's explicitly waited loads, run on the compiled device assembly.
 
 The persistent decode kernel issues its tile loads, its early q loads and its work-claim atomic
 through inline assembly, outside the compiler's wait tracking, and waits for them with explicit

@@ -3,8 +3,8 @@
 Small hand-written gfx9 assembly bodies exercise each rule: an in-flight destination register
 must not be read, copied or overwritten before a covering s_waitcnt; vmcnt retires in order;
 joins keep the most recent load; flag-guarded structurizer paths are followed only where the flag
-value allows; scalars materialised from in-flight registers may not be used.  The kernel
-assembly of this build must pass.
+value allows; scalars materialised from in-flight registers may not be used.  The library's own
+kernel assembly, as compiled from the sources, must pass.
 """
 import os
 
