@@ -1453,7 +1453,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-// Tile buffers and waves per SIMD of each kernel variant.
+// Tile buffers and waves per SIMD of each kernel variant.  Streamed 16-bit pools: five buffers, one
+// wave per SIMD (measured on the Llama-70B-class batch: 753-756 us per decode call against 761-766 us
+// with three buffers and two waves per SIMD; the MHA batch 123 against 127 us).  Streamed FP8 pools:
+// four (five do not fit beside the widening registers).  Cacheable and per-tile-policy loads (batches
+// whose rows share blocks), and fp32 pools: three buffers, two waves per SIMD, for the wider grid that
+// a batch of few long rows needs (the 20-row shared-prompt batch, every tile streamed: 92 us with three
+// buffers and two waves per SIMD against 116 us with five and one).  The defaults may be overridden at
+// compile time to measure other depths.
 #ifndef PKV_NB16
 #define PKV_NB16 5
 #endif
