@@ -48,14 +48,20 @@
 //   tiles hold 32 tokens, so that a tile has the bytes and the load widths of
 //   a 16-bit one (the QK rows are ordered so that the scores land in the
 //   operand layout of a 32-deep PV MFMA).
-// * Vector path (fp32 KV): per-token dot products with a 4-lane
-//   cross-group reduction, fp32 weights, FMA accumulation.
+// * Vector path (fp32 KV, and 16-bit KV with one query head per KV head on
+//   request): per-token dot products with a 4-lane cross-group reduction, fp32
+//   weights, FMA accumulation.
+// * Loads: streamed with the non-temporal hint by default; cacheable for a batch
+//   whose rows share blocks; or chosen per tile (cacheable inside the rows'
+//   shared prefix, streamed after it) by one scalar branch inside each group
+//   of loads, which keeps a single load sequence for the waits.
 // * q fragments live in LDS (one slot for the unit being computed, one for the
 //   unit being issued), so the tile buffers keep the registers.
 // * Online softmax in the base-2 domain (scores pre-multiplied by
-//   scale*log2(e), v_exp_f32); masked tokens get -inf scores and zeroed value
-//   elements (selected, never multiplied, so a NaN in an unused slot cannot
-//   leak in).  Rows with one partition write the output directly; longer rows
+//   scale*log2(e), v_exp_f32); the accumulators are rescaled only on tiles
+//   where some lane's running max rose (elsewhere the factor is exactly 1);
+//   masked tokens get -inf scores and zeroed value elements (selected, never
+//   multiplied, so a NaN in an unused slot cannot leak in).  Rows with one partition write the output directly; longer rows
 //   write (max, sum, acc) partials that the reduce kernel merges.
 #include <type_traits>
 
