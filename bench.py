@@ -417,7 +417,7 @@ def measured_traffic(w):
     return rec
 
 
-def roofline(res, w=None):
+def roofline(res, w=None, math="mfma"):
     n_dec, ms_dec = res.get("decode_timed", (0, 0.0))
     if not n_dec:
         return None
@@ -433,10 +433,15 @@ def roofline(res, w=None):
            # measured HBM bytes per launch: the counters' bytes-per-algorithmic-byte ratio of this
            # kernel on this workload, times this run's algorithmic bytes per launch
            "traffic": int(rec["traffic_over_algorithmic"] * per_launch) if rec else None,
-           "kernel": "decode_kernel (persistent paged decode on MFMA, "
-                     + ("FP8 E4M3 KV widened in registers" if w is not None and w.kv_format == "fp8" else "16-bit KV")
-                     + ")",
+           "kernel": kernel_label(w, math),
            "bytes_per_launch": int(per_launch), "avg_launch_us": round(avg_s * 1e6, 2)}
+    if w is not None:
+        # beside the algorithmic bytes, not counted in them: q, the output and the lengths (each once per
+        # row); and the attention's own flops, sum over rows of L * Hq * 4 * D
+        e = 4 if w.dtype == "f32" else 2
+        out["aux_bytes_per_launch"] = int(w.num_seqs * (2 * w.n_q_heads * w.head_dim * e + 4))
+        tokens = res["kv_bytes"] / res["steps"] / (2 * w.n_kv_heads * w.head_dim * w.kv_esize)
+        out["flop_per_launch"] = int(tokens * w.n_q_heads * 4 * w.head_dim)
     if logical != per_launch:
         out["achieved_logical"] = round(logical / avg_s / 1e9, 1)
         out["bytes_per_launch_logical"] = int(logical)
@@ -445,6 +450,16 @@ def roofline(res, w=None):
                                  "write_bytes": int(rec["write_over_algorithmic"] * per_launch),
                                  "source": os.path.relpath(traffic_record_path(w), ROOT)}
     return out
+
+
+def kernel_label(w, math="mfma"):
+    """Which decode kernel the roofline covers."""
+    if w is not None and w.dtype == "f32":
+        return "decode_kernel (persistent paged decode, fp32 KV on the vector path)"
+    if math == "vector":
+        return "decode_kernel (persistent paged decode, 16-bit KV on the per-token vector path)"
+    kv = "FP8 E4M3 KV widened in registers" if w is not None and w.kv_format == "fp8" else "16-bit KV"
+    return f"decode_kernel (persistent paged decode on MFMA, {kv})"
 
 
 def read_ceiling(full=False):
@@ -711,7 +726,7 @@ def main():
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(seqs_s, 1),
         "kernels": kern,
-        "roofline": roofline(res, w),
+        "roofline": roofline(res, w, args.math),
         "decode_loads": res["decode_loads"],
         "decode_math": args.math,
         "decode_launch_us": res["decode_launch_us"],

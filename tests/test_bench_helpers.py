@@ -76,3 +76,20 @@ def test_host_replay_counts_the_swarm_prompt_once_per_extra_row():
     assert bench.host_duplicate_tokens(wl.build(4, copied_prefix=True)) == 0
     assert bench.host_duplicate_tokens(wl.build(4, block_size=32)) == 19 * 4000
     assert bench.host_duplicate_tokens(wl.build(3)) == 0
+
+
+def test_roofline_reports_aux_bytes_and_flops_beside_the_algorithmic_bytes():
+    """q, the output and the lengths are reported beside the algorithmic bytes, not counted in them; the
+    attention's flops are the sum over rows of L * Hq * 4 * D."""
+    import workloads as wl
+    w = wl.build(3)
+    tokens = 1_000_000
+    kv = tokens * 2 * w.n_kv_heads * w.head_dim * 2
+    res = {"decode_timed": (10, 10 * 0.75), "kv_bytes_unique": kv * 10, "kv_bytes": kv * 10,
+           "table_bytes": 250_000 * 10, "steps": 10}
+    r = bench.roofline(res, w)
+    assert r["bytes_per_launch"] == kv + 250_000
+    assert r["aux_bytes_per_launch"] == 256 * (2 * 64 * 128 * 2 + 4)
+    assert r["flop_per_launch"] == tokens * 64 * 4 * 128
+    assert r["frac"] == pytest.approx((kv + 250_000) / 750e-6 / 1e9 / 8000.0, abs=1e-4)
+    assert "fp32 KV" in bench.kernel_label(wl.build(1)) and "MFMA" in bench.kernel_label(w)
