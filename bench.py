@@ -882,8 +882,9 @@ def sweep(args):
             if part == 512 and args.partition_size != 512:
                 key = "random_P512"
             try:
+                # (the short read probe before each point's warm-up settles the clock, as for the bench line)
                 res = time_steps(w, args.steps, args.warmup, decode_only=True, layout=layout, chunk_bytes=chunk,
-                                 reps=0)
+                                 reps=0, flush=False, before_warmup=lambda: read_ceiling(full=False))
             except RuntimeError as e:      # a span pool that cannot map this many chunks
                 per[key] = {"error": str(e)}
                 log(f"B={B} {key}: {e}")
