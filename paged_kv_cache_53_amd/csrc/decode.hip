@@ -505,8 +505,6 @@ struct Unit {
   int s, kvh, part, ntok, nparts;
   int id_first;       // the partition's first block id, read when the unit is opened
   const int32_t* bt;  // block-table row at the partition's first block
-  const T* kbase;     // k_pool + kvh * chunk
-  const T* vbase;
 };
 
 // FLAT: the row's blocks are the consecutive blocks of its span (block_tables holds one span index
@@ -532,8 +530,7 @@ __device__ inline Unit<T> open_unit(const DecodeArgs& a, int id, int64_t chunk) 
   } else {
     u.bt = a.block_tables + static_cast<int64_t>(u.s) * a.bt_stride + (tok0 >> a.log2_block);
   }
-  u.kbase = static_cast<const T*>(a.k_pool) + static_cast<int64_t>(u.kvh) * chunk;
-  u.vbase = static_cast<const T*>(a.v_pool) + static_cast<int64_t>(u.kvh) * chunk;
+  (void)chunk;
   return u;
 }
 
@@ -1346,7 +1343,8 @@ void decode_kernel(DecodeArgs a) {
     }
     Y.template issue<Bsz, E, NT, FLAT, MIX>(a, is_real ? +ui.bt : +uc.bt, is_real ? +ui.id_first : +uc.id_first,
                                       is_real ? +ui.ntok : +uc.ntok,
-                                      is_real ? +ui.kbase : +uc.kbase, is_real ? +ui.vbase : +uc.vbase,
+                                      static_cast<const KV*>(a.k_pool) + static_cast<int64_t>(is_real ? +ui.kvh : +uc.kvh) * chunk,
+                                      static_cast<const KV*>(a.v_pool) + static_cast<int64_t>(is_real ? +ui.kvh : +uc.kvh) * chunk,
                                       is_real ? +ti : tc_now, blk_stride, cached);
     ti += is_real ? TT : 0;   // a select: a conditional update would put ti in memory
     return is_real;
