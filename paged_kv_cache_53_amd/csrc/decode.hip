@@ -64,6 +64,7 @@
 //   multiplied, so a NaN in an unused slot cannot leak in).  Rows with one partition write the output directly; longer rows
 //   write (max, sum, acc) partials that the reduce kernel merges.
 #include <type_traits>
+#include <utility>
 
 #include "pkv_internal.h"
 #include "scatter_body.h"
@@ -375,6 +376,34 @@ __device__ inline void vload(unsigned& d, const void* p) {
   else if constexpr (NT) d = __builtin_nontemporal_load(static_cast<const unsigned*>(p));
   else d = *static_cast<const unsigned*>(p);
 }
+// The loads of a tile at constant byte strides from one address: the strides go into the
+// instructions' immediate offsets (at most 4095 bytes), so the group needs one address register pair
+// instead of one per load.  Larger strides keep one address per load.
+template <bool E, bool NT, int OFF>
+__device__ inline void vload_at(u32x4& d, const void* p) {
+  if constexpr (E && NT) asm volatile("global_load_dwordx4 %0, %1, off offset:%2 nt" : "+v"(d) : "v"(p), "i"(OFF));
+  else if constexpr (E) asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "+v"(d) : "v"(p), "i"(OFF));
+  else vload<E, NT>(d, static_cast<const char*>(p) + OFF);
+}
+template <bool E, bool NT, int OFF>
+__device__ inline void vload_at(u32x2& d, const void* p) {
+  if constexpr (E && NT) asm volatile("global_load_dwordx2 %0, %1, off offset:%2 nt" : "+v"(d) : "v"(p), "i"(OFF));
+  else if constexpr (E) asm volatile("global_load_dwordx2 %0, %1, off offset:%2" : "+v"(d) : "v"(p), "i"(OFF));
+  else vload<E, NT>(d, static_cast<const char*>(p) + OFF);
+}
+template <bool E, bool NT, int STRIDE, typename Dst, size_t... I>
+__device__ inline void vload_strided_seq(Dst* d, const void* p, std::index_sequence<I...>) {
+  if constexpr ((sizeof...(I) - 1) * STRIDE <= 4095) {
+    (vload_at<E, NT, static_cast<int>(I) * STRIDE>(d[I], p), ...);
+  } else {
+    (vload<E, NT>(d[I], static_cast<const char*>(p) + static_cast<int>(I) * STRIDE), ...);
+  }
+}
+template <bool E, bool NT, int STRIDE, int N, typename Dst>
+__device__ inline void vload_strided(Dst (&d)[N], const void* p) {
+  vload_strided_seq<E, NT, STRIDE>(d, p, std::make_index_sequence<N>{});
+}
+
 // Per-tile choice of the load policy: a group of loads issued in one asm statement whose one scalar
 // branch picks the cacheable or the non-temporal form of every load (cached: wave-uniform, nonzero for
 // cacheable).  Both paths issue the same loads into the same registers, so the statement counts the
@@ -573,8 +602,7 @@ struct Tile16 {
       for (int ks = 0; ks < NK; ++ks) ka[ks] = kb + ks * 4 * Bsz * X;
       vload_group(kf, ka, cached);
     } else {
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) vload<E, NT>(kf[ks], kb + ks * 4 * Bsz * X);
+      vload_strided<E, NT, 4 * Bsz * X * static_cast<int>(sizeof(T))>(kf, kb);
     }
     const int bv = (NB == 2 && g >= 2) ? id1 : id0;
     const T* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((t0 + 4 * g) & (Bsz - 1));
@@ -589,8 +617,7 @@ struct Tile16 {
       for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
       vload_group(vf, va, Bsz <= 16 ? cached : 1u);
     } else {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) vload<E, kNTV>(vf[dt], vb + dt * 16 * Bsz);
+      vload_strided<E, kNTV, 16 * Bsz * static_cast<int>(sizeof(T))>(vf, vb);
     }
   }
   // orders every later use of the tile's registers after the preceding wait
@@ -649,10 +676,11 @@ struct Tile32F8 {
 #pragma unroll
       for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
       const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + (tt & (Bsz - 1))) * 16;
+      if constexpr (MIX) {
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        ka[b * NK + ks] = kb + ks * 4 * Bsz * 16;
-        if constexpr (!MIX) vload<E, NT>(kf[b][ks], ka[b * NK + ks]);
+        for (int ks = 0; ks < NK; ++ks) ka[b * NK + ks] = kb + ks * 4 * Bsz * 16;
+      } else {
+        vload_strided<E, NT, 4 * Bsz * 16>(kf[b], kb);
       }
     }
     if constexpr (MIX) {
@@ -671,8 +699,7 @@ struct Tile32F8 {
       for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
       vload_group(vf, va, cached);
     } else {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) vload<E, NT>(vf[dt], vb + dt * 16 * Bsz);
+      vload_strided<E, NT, 16 * Bsz>(vf, vb);
     }
   }
   template <bool E> __device__ void tie_all() {
