@@ -505,6 +505,89 @@ template <int N> __device__ inline void vload_group(u32x2 (&d)[N], const void* c
   else vload_sel(d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7], p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], c);
 }
 
+// vload_group for loads at constant byte strides from one address (immediate offsets, at most 4095
+// bytes): one address register pair for the whole group.
+template <int S>
+__device__ inline void vload_sel_strided(u32x4 (&d)[2], const void* p, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %3, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx4 %0, %2, off\n\t"
+      "global_load_dwordx4 %1, %2, off offset:%4\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx4 %0, %2, off nt\n\t"
+      "global_load_dwordx4 %1, %2, off offset:%4 nt\n"
+      "2:"
+      : "+v"(d[0]), "+v"(d[1])
+      : "v"(p), "s"(c), "i"(S)
+      : "scc");
+}
+template <int S>
+__device__ inline void vload_sel_strided(u32x4 (&d)[4], const void* p, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %5, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx4 %0, %4, off\n\t"
+      "global_load_dwordx4 %1, %4, off offset:%6\n\t"
+      "global_load_dwordx4 %2, %4, off offset:%7\n\t"
+      "global_load_dwordx4 %3, %4, off offset:%8\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx4 %0, %4, off nt\n\t"
+      "global_load_dwordx4 %1, %4, off offset:%6 nt\n\t"
+      "global_load_dwordx4 %2, %4, off offset:%7 nt\n\t"
+      "global_load_dwordx4 %3, %4, off offset:%8 nt\n"
+      "2:"
+      : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3])
+      : "v"(p), "s"(c), "i"(S), "i"(2 * S), "i"(3 * S)
+      : "scc");
+}
+template <int S>
+__device__ inline void vload_sel_strided(u32x2 (&d)[8], const void* p, unsigned cached) {
+  const unsigned c = __builtin_amdgcn_readfirstlane(cached);   // (a scalar operand)
+  asm volatile(
+      "s_cmp_eq_u32 %9, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_dwordx2 %0, %8, off\n\t"
+      "global_load_dwordx2 %1, %8, off offset:%10\n\t"
+      "global_load_dwordx2 %2, %8, off offset:%11\n\t"
+      "global_load_dwordx2 %3, %8, off offset:%12\n\t"
+      "global_load_dwordx2 %4, %8, off offset:%13\n\t"
+      "global_load_dwordx2 %5, %8, off offset:%14\n\t"
+      "global_load_dwordx2 %6, %8, off offset:%15\n\t"
+      "global_load_dwordx2 %7, %8, off offset:%16\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_dwordx2 %0, %8, off nt\n\t"
+      "global_load_dwordx2 %1, %8, off offset:%10 nt\n\t"
+      "global_load_dwordx2 %2, %8, off offset:%11 nt\n\t"
+      "global_load_dwordx2 %3, %8, off offset:%12 nt\n\t"
+      "global_load_dwordx2 %4, %8, off offset:%13 nt\n\t"
+      "global_load_dwordx2 %5, %8, off offset:%14 nt\n\t"
+      "global_load_dwordx2 %6, %8, off offset:%15 nt\n\t"
+      "global_load_dwordx2 %7, %8, off offset:%16 nt\n"
+      "2:"
+      : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]), "+v"(d[7])
+      : "v"(p), "s"(c), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S), "i"(7 * S)
+      : "scc");
+}
+// the strided group where its offsets fit the instructions, else one address per load
+template <int S, int N, typename Dst>
+__device__ inline void vload_group_strided(Dst (&d)[N], const void* p, unsigned cached) {
+  if constexpr ((N - 1) * S <= 4095 && (N == 2 || N == 4 || N == 8) &&
+                (std::is_same<Dst, u32x4>::value ? N != 8 : N == 8)) {
+    vload_sel_strided<S>(d, p, cached);
+  } else {
+    const void* a[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = static_cast<const char*>(p) + i * S;
+    vload_group(d, a, cached);
+  }
+}
+
 // waits until at most N vector-memory operations are outstanding
 // (the memory clobber keeps every memory access of the source on its side of the wait: a read of
 // LDS that a global-to-LDS load fills must not be scheduled above the wait that retires that load)
@@ -597,10 +680,7 @@ struct Tile16 {
     const int bk = (NB == 2 && r16 >= 8) ? id1 : id0;
     const T* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (((t0 + r16) & (Bsz - 1)) + g * Bsz) * X;
     if constexpr (MIX) {
-      const void* ka[NK];
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) ka[ks] = kb + ks * 4 * Bsz * X;
-      vload_group(kf, ka, cached);
+      vload_group_strided<4 * Bsz * X * static_cast<int>(sizeof(T))>(kf, kb, cached);
     } else {
       vload_strided<E, NT, 4 * Bsz * X * static_cast<int>(sizeof(T))>(kf, kb);
     }
@@ -612,10 +692,7 @@ struct Tile16 {
     // instead of 840 us on the Llama-70B-class batch at B = 32).  Key lines are read whole.
     constexpr bool kNTV = NT && Bsz <= 16;
     if constexpr (MIX) {
-      const void* va[D / 16];
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
-      vload_group(vf, va, Bsz <= 16 ? cached : 1u);
+      vload_group_strided<16 * Bsz * static_cast<int>(sizeof(T))>(vf, vb, Bsz <= 16 ? cached : 1u);
     } else {
       vload_strided<E, kNTV, 16 * Bsz * static_cast<int>(sizeof(T))>(vf, vb);
     }
@@ -676,14 +753,15 @@ struct Tile32F8 {
 #pragma unroll
       for (int j = 1; j < NB; ++j) bk = jk == j ? id[j] : bk;
       const E4M3* kb = kbase + static_cast<int64_t>(bk) * blk_stride + (g * Bsz + (tt & (Bsz - 1))) * 16;
-      if constexpr (MIX) {
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) ka[b * NK + ks] = kb + ks * 4 * Bsz * 16;
+      if constexpr (MIX && NK == 1) {
+        ka[b] = kb;   // one load per row block: both row blocks in one group below
+      } else if constexpr (MIX) {
+        vload_group_strided<4 * Bsz * 16>(kf[b], kb, cached);
       } else {
         vload_strided<E, NT, 4 * Bsz * 16>(kf[b], kb);
       }
     }
-    if constexpr (MIX) {
+    if constexpr (MIX && NK == 1) {
       u32x4(&kflat)[2 * NK] = *reinterpret_cast<u32x4(*)[2 * NK]>(&kf[0][0]);
       vload_group(kflat, ka, cached);
     }
@@ -694,10 +772,7 @@ struct Tile32F8 {
     for (int j = 1; j < NB; ++j) bv = jv == j ? id[j] : bv;
     const E4M3* vb = vbase + static_cast<int64_t>(bv) * blk_stride + r16 * Bsz + ((8 * g) & (Bsz - 1));
     if constexpr (MIX) {
-      const void* va[D / 16];
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) va[dt] = vb + dt * 16 * Bsz;
-      vload_group(vf, va, cached);
+      vload_group_strided<16 * Bsz>(vf, vb, cached);
     } else {
       vload_strided<E, NT, 16 * Bsz>(vf, vb);
     }
