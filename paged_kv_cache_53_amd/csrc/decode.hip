@@ -1095,6 +1095,53 @@ struct MfmaMath {
       for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x32(widen8<T>(R.vf[dt][0], R.vf[dt][1]), pb, acc[dt]);
     }
   }
+  // A finished unit's results parked in LDS until the wave has no more units: the normalised
+  // output of a one-partition row (part < 0), else the partition's (max, sum, accumulator).  For
+  // groups of at most 8 heads: lane 16k + r holds head r, so lane r + 8g of an entry's 32 is
+  // written by lane 16g + r.
+  static constexpr bool kPark = true;
+  struct Parked {
+    f32x4 acc[D / 16][32];
+    float m[8], l[8];
+    int row0, part;
+  };
+  // the same values finish() stores, into LDS
+  __device__ void park(const DecodeArgs& a, const Unit<KV>& u, Parked& p) {
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const float l_tot = sum_x32(sum_x16(l_run));
+    if (threadIdx.x == 0) {
+      p.row0 = u.s * a.n_q_heads + u.kvh * a.group;
+      p.part = u.nparts == 1 ? -1 : u.part;
+    }
+    if (r16 >= 8) return;
+    const float sc = u.nparts == 1 ? (kQuant ? a.v_scale / l_tot : 1.f / l_tot) : (kQuant ? a.v_scale : 1.f);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) p.acc[dt][8 * g + r16] = acc[dt] * sc;
+    if (g == 0) {
+      p.m[r16] = m_run;
+      p.l[r16] = l_tot;
+    }
+  }
+  // writes a parked unit's results where finish() would have
+  __device__ static void unpark(const DecodeArgs& a, const Parked& p) {
+    const int r16 = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int row0 = __builtin_amdgcn_readfirstlane(p.row0);
+    const int part = __builtin_amdgcn_readfirstlane(p.part);
+    if (r16 >= a.group) return;
+    const int64_t row = row0 + r16;
+    if (part < 0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) store4<T>(a.out, row * D + 16 * dt + 4 * g, p.acc[dt][8 * g + r16], a.out_f32);
+    } else {
+      const int64_t pidx = row * a.max_parts + part;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) st_wt(a.part_acc + pidx * D + 16 * dt + 4 * g, p.acc[dt][8 * g + r16]);
+      if (g == 0) {
+        st_wt(a.part_m + pidx, p.m[r16]);
+        st_wt(a.part_l + pidx, p.l[r16]);
+      }
+    }
+  }
   // the normalised output when the row has one partition, else (max, sum, accumulator); with
   // quantised values the accumulator is scaled by the value scale
   __device__ void finish(const DecodeArgs& a, const Unit<KV>& u) {
@@ -1126,6 +1173,8 @@ struct MfmaMath {
 // 16dt + lane%16 over tokens 4g..4g+3, summed over the 4 groups when the unit ends).
 template <typename T, int D, int GM>
 struct VecMath {
+  static constexpr bool kPark = false;   // results are stored as each unit ends
+  struct Parked {};
   static constexpr int QH = GM;
   static constexpr bool kPrefetchQ = GM == 1;   // more heads: q is loaded at the unit switch
   static constexpr bool kGroup = true;
@@ -1340,6 +1389,20 @@ void decode_kernel(DecodeArgs a) {
   const int64_t blk_stride = chunk * a.n_kv_heads;
   const int total = ld_uniform(a.counters, 0) * a.n_kv_heads;
   __shared__ u32x4 q_lds[2][Math::QH][NQ][64];   // q fragments: compute unit's and issue unit's
+  // Finished units' results wait in LDS while the wave reads on, and are written out when it has no
+  // more units: result stores in the middle of the read stream slowed every wave (on the
+  // Llama-70B-class batch the mean wave end fell 730 -> 717 us at P 3072 and 756 -> 722 us at
+  // P 1536 once they moved to the end).  As many entries as fit beside q in this wave's share of
+  // the CU's 160 KB; a unit that finds them full stores its results at once.  (FP8 pools in 8-token
+  // blocks store at once: with parking, that kernel's register allocation failed the wait check.)
+  using Parked = typename Math::Parked;
+  constexpr int kLdsShare = 160 * 1024 / (4 * WPE);
+  constexpr bool kParkHere = Math::kPark && !(sizeof(KV) == 1 && Bsz == 8);
+  constexpr int NPARK = kParkHere ? static_cast<int>((kLdsShare - static_cast<int>(sizeof(q_lds)) - 512) /
+                                                       static_cast<int>(sizeof(Parked)))
+                                    : 0;
+  __shared__ Parked parked[NPARK > 0 ? NPARK : 1];
+  int n_parked = 0;
 
   // Each wave starts on one of the grid's first units, and the counter hands out the units after
   // them: every wave claiming its first unit from the one counter at once serialised 2048 atomics
@@ -1478,7 +1541,16 @@ void decode_kernel(DecodeArgs a) {
     mt.compute(X, q_lds[slot_c], tc, uc.ntok, scale_log2);
     tc += TT;
     if (tc < uc.ntok) return true;
-    mt.finish(a, uc);
+    if constexpr (NPARK > 0) {
+      if (a.group <= 8 && n_parked < NPARK) {
+        mt.park(a, uc, parked[n_parked]);
+        ++n_parked;
+      } else {
+        mt.finish(a, uc);
+      }
+    } else {
+      mt.finish(a, uc);
+    }
     if (!(fl & kAhead)) return false;   // the issue side found no further unit: every issued tile is filler
     uc = ui;
     slot_c = slot_i;
@@ -1508,6 +1580,9 @@ void decode_kernel(DecodeArgs a) {
   else if constexpr (NB == 5) steps(I0{}, I1{}, I2{}, I3{}, I4{});
   else steps(I0{}, I1{}, I2{}, I3{}, I4{}, I5{});
   vm_wait<E, 0>();   // filler loads still in flight land before the wave ends
+  if constexpr (NPARK > 0) {
+    for (int k = 0; k < n_parked; ++k) Math::unpark(a, parked[k]);
+  }
 }
 
 // ------------------------------------------------------------------------------ merge
