@@ -166,7 +166,7 @@ def oracle_all(w: wl.Workload) -> np.ndarray:
     distinct set of values.  Block size, placement, partition size and shared-vs-copied prompts
     change where rows are stored, never their logical values, so those do not enter the key."""
     key = (w.name, w.seed, w.variant.replace("-copied", "").replace("-shared", ""), w.kv_format,
-           w.k_scale, w.v_scale, tuple(w.seq_lens.tolist()))
+           w.k_scale, w.v_scale, tuple(w.seq_lens.tolist()), w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype)
     if key not in _ORACLE_CACHE:
         t0 = time.time()
         ref = oracle_rows(w, range(w.num_seqs))
